@@ -1,0 +1,313 @@
+"""Pins of the f64 CPU oracle to things other than itself (CPU only).
+
+Each check is chosen so that a plausible slip in oracle/attn_oracle.c -- a dropped term, a wrong
+sign, a transposed operand, a mask off by one, the wrong lse base, the wrong GQA head mapping,
+a duplicate top-k entry counted once -- fails at least one of them:
+  * central finite differences of L = sum(O * dO) (O from the f64 forward),
+  * torch float64 autograd of an explicitly masked natural-base softmax attention,
+  * a brute-force dense numpy restatement (tests/bruteforce.py),
+  * the softmax-gradient invariants (dS rows sum to 0, so the dK columns do; dV = P^T dO;
+    dV columns sum to the dO of live rows; delta = sum_j p dp),
+  * closed forms (window 1, constant V, Q = 0, shifted keys) and reductions to simpler cases
+    (window >= S is causal, a top-k list of every allowed key is dense causal, GQA is MHA on
+    repeated K/V, masked keys change nothing).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import forward as oracle_forward
+from tests import bruteforce as bf
+
+LOG2E = 1.4426950408889634
+
+
+def rnd(seed, B, Sq, Skv, Hq, Hkv, Dqk, Dv):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((B, Sq, Hq, Dqk))
+    k = r.standard_normal((B, Skv, Hkv, Dqk))
+    v = r.standard_normal((B, Skv, Hkv, Dv))
+    do = r.standard_normal((B, Sq, Hq, Dv))
+    return q, k, v, do
+
+
+def rnd_idx(seed, B, Sq, Skv, Hkv, topk, pad=True, dup=True):
+    """Random top-k lists with -1 padding, out-of-range, non-causal and duplicate entries."""
+    r = np.random.default_rng(seed)
+    idx = r.integers(0, Skv, size=(B, Sq, Hkv, topk)).astype(np.int32)
+    if pad:
+        idx[..., -1] = -1
+        idx[..., 0] = Skv + 3  # out of range: masked
+    if dup and topk > 3:
+        idx[..., 2] = idx[..., 1]
+    return idx
+
+
+def loss(q, k, v, do, scale, causal, window, idx=None):
+    o, _ = oracle.fwd(q, k, v, scale, causal, window, idx)
+    return float((o * do).sum())
+
+
+CASES = [
+    # B, Sq, Skv, Hq, Hkv, Dqk, Dv, causal, window, sparse
+    (1, 7, 7, 4, 2, 4, 4, True, 0, False),
+    (2, 9, 9, 4, 1, 8, 6, True, 0, False),
+    (1, 3, 9, 4, 4, 4, 4, True, 0, False),     # Sq < Skv: bottom-right alignment
+    (1, 9, 3, 4, 2, 4, 4, True, 0, False),     # Sq > Skv: rows with no key
+    (2, 7, 7, 4, 2, 8, 6, False, 0, False),
+    (1, 9, 9, 4, 2, 4, 4, True, 3, False),
+    (1, 9, 9, 4, 4, 4, 4, True, 1, False),
+    (2, 7, 9, 4, 1, 8, 6, True, 0, True),
+    (1, 9, 9, 4, 2, 4, 4, False, 0, True),
+]
+
+
+def case_inputs(c, seed=0):
+    B, Sq, Skv, Hq, Hkv, Dqk, Dv, causal, window, sparse = c
+    q, k, v, do = rnd(seed, B, Sq, Skv, Hq, Hkv, Dqk, Dv)
+    idx = rnd_idx(seed + 1, B, Sq, Skv, Hkv, 6) if sparse else None
+    return q, k, v, do, idx, 1.0 / math.sqrt(Dqk), causal, window
+
+
+@pytest.mark.parametrize("c", CASES)
+def test_finite_differences(c):
+    q, k, v, do, idx, scale, causal, window = case_inputs(c)
+    o, lse = oracle.fwd(q, k, v, scale, causal, window, idx)
+    dq, dk, dv = oracle.bwd(q, k, v, o, do, lse, scale, causal, window, idx)
+    h = 1e-6
+    r = np.random.default_rng(7)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        flat = x.reshape(-1)
+        picks = r.choice(flat.size, size=min(flat.size, 24), replace=False)
+        for p in picks:
+            keep = flat[p]
+            flat[p] = keep + h
+            lp = loss(q, k, v, do, scale, causal, window, idx)
+            flat[p] = keep - h
+            lm = loss(q, k, v, do, scale, causal, window, idx)
+            flat[p] = keep
+            fd = (lp - lm) / (2 * h)
+            an = g.reshape(-1)[p]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, p, fd, an)
+
+
+def torch_autograd(q, k, v, do, scale, causal, window, idx):
+    """Natural-base softmax attention with an explicit multiplicity mask, differentiated by torch."""
+    B, Sq, Hq, _ = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    kr = tk.repeat_interleave(G, dim=2)  # [B,Skv,Hq,D]: query head h reads kv head h // G
+    vr = tv.repeat_interleave(G, dim=2)
+    out = []
+    for b in range(B):
+        heads = []
+        for h in range(Hq):
+            M = torch.tensor(bf.multiplicity(Sq, Skv, causal, window, None if idx is None else idx[b, :, h // G, :]))
+            s = tq[b, :, h, :] @ kr[b, :, h, :].T * scale + torch.log(M)  # log 0 = -inf masks
+            has = (M.sum(1) > 0).unsqueeze(1)
+            p = torch.softmax(torch.where(has, s, torch.zeros_like(s)), dim=1) * has
+            heads.append(p @ vr[b, :, h, :])
+        out.append(torch.stack(heads, dim=1))
+    o = torch.stack(out, 0)
+    (o * torch.tensor(do)).sum().backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("c", CASES)
+def test_torch_autograd(c):
+    q, k, v, do, idx, scale, causal, window = case_inputs(c, seed=3)
+    o, lse = oracle.fwd(q, k, v, scale, causal, window, idx)
+    got = oracle.bwd(q, k, v, o, do, lse, scale, causal, window, idx)
+    want = torch_autograd(q, k, v, do, scale, causal, window, idx)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("c", CASES)
+def test_bruteforce_dense(c):
+    q, k, v, do, idx, scale, causal, window = case_inputs(c, seed=5)
+    o, lse = oracle.fwd(q, k, v, scale, causal, window, idx)
+    bo, blse = bf.forward(q, k, v, scale, causal, window, idx)
+    np.testing.assert_allclose(o, bo, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(np.isinf(lse), np.isinf(blse))
+    np.testing.assert_allclose(lse[np.isfinite(lse)], blse[np.isfinite(blse)], rtol=1e-12, atol=1e-12)
+    # inconsistent O (rounded to fp16) is what the backward really receives: still must agree
+    o16 = o.astype(np.float16).astype(np.float64)
+    lse32 = lse.astype(np.float32).astype(np.float64)
+    got = oracle.bwd(q, k, v, o16, do, lse32, scale, causal, window, idx)
+    want = bf.backward(q, k, v, o16, do, lse32, scale, causal, window, idx)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(oracle.delta(o16, do), np.einsum("bihd,bihd->bhi", o16, do), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("c", CASES)
+def test_invariants(c):
+    q, k, v, do, idx, scale, causal, window = case_inputs(c, seed=9)
+    B, Sq, Skv, Hq, Hkv = q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2]
+    G = Hq // Hkv
+    o, lse = oracle.fwd(q, k, v, scale, causal, window, idx)
+    dq, dk, dv = oracle.bwd(q, k, v, o, do, lse, scale, causal, window, idx)
+    _, _, _, ps = bf.backward(q, k, v, o, do, lse, scale, causal, window, idx, return_p=True)
+    delta = oracle.delta(o, do)
+    for b in range(B):
+        for g in range(Hkv):
+            # dK column sums vanish because every dS row sums to zero
+            tot = np.zeros(q.shape[3])
+            scale_abs = 0.0
+            dv_want = np.zeros(v.shape[3])
+            pt_do = np.zeros((Skv, v.shape[3]))
+            for h in range(g * G, (g + 1) * G):
+                p, dp, ds, dl = ps[(b, h)]
+                live = p.sum(1) > 0
+                np.testing.assert_allclose(p[live].sum(1), 1.0, rtol=1e-12)
+                np.testing.assert_allclose(ds.sum(1), 0.0, atol=1e-12 * max(1.0, np.abs(ds).sum()))
+                np.testing.assert_allclose(delta[b, h][live], (p * dp).sum(1)[live], rtol=1e-10, atol=1e-12)
+                scale_abs += np.abs(scale * ds.T @ q[b, :, h, :]).sum()
+                dv_want += do[b, live, h, :].sum(0)
+                pt_do += p.T @ do[b, :, h, :]
+            np.testing.assert_allclose(dk[b, :, g, :].sum(0), 0.0, atol=1e-12 * max(1.0, scale_abs))
+            np.testing.assert_allclose(dv[b, :, g, :].sum(0), dv_want, rtol=1e-11, atol=1e-11)
+            np.testing.assert_allclose(dv[b, :, g, :], pt_do, rtol=1e-12, atol=1e-12)
+
+
+def test_window_one_and_single_key_closed_form():
+    for (Sq, causal, window) in ((9, True, 1), (1, True, 0), (1, False, 0)):
+        q, k, v, do = rnd(11, 2, Sq, Sq, 4, 2, 8, 6)
+        scale = 0.3
+        o, lse = oracle.fwd(q, k, v, scale, causal, window)
+        dq, dk, dv = oracle.bwd(q, k, v, o, do, lse, scale, causal, window)
+        assert np.all(dq == 0.0) and np.all(dk == 0.0)
+        want = do.reshape(2, Sq, 2, 2, 6).sum(3)  # sum over the G=2 query heads of each kv head
+        np.testing.assert_array_equal(dv, want)
+
+
+def test_constant_v_and_zero_q_closed_forms():
+    B, S, Hq, Hkv, D = 1, 9, 4, 2, 8
+    q, k, v, do = rnd(13, B, S, S, Hq, Hkv, D, D)
+    vc = np.broadcast_to(v[:, :1], v.shape).copy()
+    o, lse = oracle.fwd(q, k, vc, 0.4, True, 0)
+    dq, dk, _ = oracle.bwd(q, k, vc, o, do, lse, 0.4, True, 0)
+    assert np.abs(dq).max() < 1e-13 and np.abs(dk).max() < 1e-13
+    # Q = 0: uniform p = 1/(i+1) over the causal prefix
+    qz = np.zeros_like(q)
+    o, lse = oracle.fwd(qz, k, v, 0.4, True, 0)
+    _, _, dv = oracle.bwd(qz, k, v, o, do, lse, 0.4, True, 0)
+    want = np.zeros_like(dv)
+    for j in range(S):
+        for i in range(j, S):
+            for h in range(Hq):
+                want[0, j, h // 2] += do[0, i, h] / (i + 1)
+    np.testing.assert_allclose(dv, want, rtol=1e-13, atol=1e-14)
+
+
+def test_key_shift_leaves_dq_unchanged():
+    q, k, v, do = rnd(17, 1, 9, 9, 4, 2, 8, 8)
+    u = np.random.default_rng(1).standard_normal(8)
+    o, lse = oracle.fwd(q, k, v, 0.35, True, 0)
+    dq0, _, _ = oracle.bwd(q, k, v, o, do, lse, 0.35, True, 0)
+    k2 = k + u
+    o2, lse2 = oracle.fwd(q, k2, v, 0.35, True, 0)
+    dq1, _, _ = oracle.bwd(q, k2, v, o2, do, lse2, 0.35, True, 0)
+    np.testing.assert_allclose(dq1, dq0, rtol=1e-10, atol=1e-12)
+
+
+def test_reductions_to_simpler_cases():
+    q, k, v, do = rnd(19, 2, 11, 11, 4, 2, 8, 8)
+    s = 0.3
+    o, lse = oracle.fwd(q, k, v, s, True, 0)
+    ref = oracle.bwd(q, k, v, o, do, lse, s, True, 0)
+    # window >= S is plain causal (bit-identical: same key sets, same order)
+    ow, lw = oracle.fwd(q, k, v, s, True, 11)
+    np.testing.assert_array_equal(ow, o)
+    for a, b in zip(oracle.bwd(q, k, v, o, do, lse, s, True, 11), ref):
+        np.testing.assert_array_equal(a, b)
+    # a top-k list holding exactly the causal keys (padded with -1) is dense causal
+    idx = np.full((2, 11, 2, 11), -1, np.int32)
+    for i in range(11):
+        idx[:, i, :, : i + 1] = np.arange(i + 1)[::-1]
+    os_, ls_ = oracle.fwd(q, k, v, s, True, 0, idx)
+    np.testing.assert_allclose(os_, o, rtol=1e-13, atol=1e-14)
+    for a, b in zip(oracle.bwd(q, k, v, o, do, lse, s, True, 0, idx), ref):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+    # GQA equals MHA on K/V repeated per query head, with dK/dV summed over each group
+    kr, vr = np.repeat(k, 2, axis=2), np.repeat(v, 2, axis=2)
+    dqm, dkm, dvm = oracle.bwd(q, kr, vr, o, do, lse, s, True, 0)
+    np.testing.assert_allclose(dqm, ref[0], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dkm.reshape(2, 11, 2, 2, 8).sum(3), ref[1], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dvm.reshape(2, 11, 2, 2, 8).sum(3), ref[2], rtol=1e-12, atol=1e-13)
+
+
+def test_masked_keys_change_nothing():
+    s = 0.3
+    # dense: Sq=4 queries over Skv=12 keys, causal (bottom-right) with a window of 3 keys:
+    # query i sees keys i+6..i+8, so keys 0..5 are outside every allowed set
+    q, k, v, do = rnd(23, 1, 4, 12, 4, 2, 8, 8)
+    o, lse = oracle.fwd(q, k, v, s, True, 3)
+    a = oracle.bwd(q, k, v, o, do, lse, s, True, 3)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :6] = 1e3
+    v2[:, :6] = -1e3
+    b = oracle.bwd(q, k2, v2, o, do, lse, s, True, 3)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    assert np.all(a[1][:, :6] == 0.0) and np.all(a[2][:, :6] == 0.0)
+    # sparse: a list that never names keys 1,3,5.. (with padding, a duplicate and out-of-range)
+    q, k, v, do = rnd(24, 1, 12, 12, 4, 2, 8, 8)
+    idx = np.tile(np.array([0, 2, 4, 4, -1, 99], np.int32), (1, 12, 2, 1))
+    o, lse = oracle.fwd(q, k, v, s, True, 0, idx)
+    a = oracle.bwd(q, k, v, o, do, lse, s, True, 0, idx)
+    never = [1, 3, 5, 6, 7, 8, 9, 10, 11]
+    k2, v2 = k.copy(), v.copy()
+    k2[:, never] = 1e3
+    v2[:, never] = -1e3
+    b = oracle.bwd(q, k2, v2, o, do, lse, s, True, 0, idx)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    assert np.all(a[1][:, never] == 0.0) and np.all(a[2][:, never] == 0.0)
+
+
+def test_rows_entry_points_match_full():
+    for c in CASES:
+        q, k, v, do, idx, scale, causal, window = case_inputs(c, seed=29)
+        o, lse = oracle.fwd(q, k, v, scale, causal, window, idx)
+        dq, dk, dv = oracle.bwd(q, k, v, o, do, lse, scale, causal, window, idx)
+        B, Sq, Hq = q.shape[:3]
+        Skv, Hkv = k.shape[1:3]
+        rows = np.array([(b, i, h) for b in range(B) for i in range(Sq) for h in range(Hq)])
+        np.testing.assert_array_equal(oracle.bwd_dq_rows(q, k, v, o, do, lse, scale, rows, causal, window, idx),
+                                      dq.reshape(-1, q.shape[3]))
+        krows = np.array([(b, j, g) for b in range(B) for j in range(Skv) for g in range(Hkv)])
+        a, b_ = oracle.bwd_dkv_rows(q, k, v, o, do, lse, scale, krows, causal, window, idx)
+        np.testing.assert_array_equal(a, dk.reshape(-1, k.shape[3]))
+        np.testing.assert_array_equal(b_, dv.reshape(-1, v.shape[3]))
+
+
+@pytest.mark.parametrize("c", CASES)
+def test_torch_forward_matches_c_forward(c):
+    q, k, v, do, idx, scale, causal, window = case_inputs(c, seed=31)
+    o, lse = oracle.fwd(q, k, v, scale, causal, window, idx)
+    t = lambda a: torch.from_numpy(a)  # noqa: E731
+    to, tl = oracle_forward.fwd(t(q), t(k), t(v), scale, causal, window, None if idx is None else t(idx), rows=4)
+    np.testing.assert_allclose(to.numpy(), o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(np.isinf(tl.numpy()), np.isinf(lse))
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(tl.numpy()[fin], lse[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_lse_minus_inf_row_contributes_nothing():
+    q, k, v, do = rnd(37, 1, 6, 6, 2, 2, 4, 4)
+    o, lse = oracle.fwd(q, k, v, 0.5, True, 0)
+    lse2 = lse.copy()
+    lse2[0, 1, 3] = -np.inf
+    dq, dk, dv = oracle.bwd(q, k, v, o, do, lse2, 0.5, True, 0)
+    assert np.all(dq[0, 3, 1] == 0.0)
+    ref = bf.backward(q, k, v, o, do, lse2, 0.5, True, 0)
+    for a, b in zip((dq, dk, dv), ref):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
