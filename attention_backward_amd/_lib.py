@@ -1,0 +1,154 @@
+"""ctypes binding of libattn_bwd.so -- argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/attn_bwd.h) and does
+nothing but check that torch tensors are on the GPU, contiguous and of the right dtype, and
+pass their device pointers, the sizes and torch's current HIP stream.  All arithmetic runs in
+the library's kernels.  There is no fallback: if the library is missing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_bwd.so")
+
+ATTN_DT_F16, ATTN_DT_BF16 = 0, 1
+ATTN_OK, ATTN_E_INVAL, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = 0, -1, -2, -3, -4
+_DT = {torch.float16: ATTN_DT_F16, torch.bfloat16: ATTN_DT_BF16}
+
+EXPORTS = ("attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_size", "attn_bwd_delta", "attn_bwd_strerror")
+
+
+class attn_bwd_args(ctypes.Structure):  # noqa: N801  (mirrors the C struct name)
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("dout", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("topk_idx", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("B", ctypes.c_int64), ("Sq", ctypes.c_int64), ("Skv", ctypes.c_int64), ("Hq", ctypes.c_int64),
+        ("Hkv", ctypes.c_int64), ("Dqk", ctypes.c_int64), ("Dv", ctypes.c_int64), ("topk", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+        ("events", ctypes.c_void_p),
+    ]
+
+
+class AttnBwdError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"attn_bwd status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_backward_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        lib.attn_bwd_workspace_size.argtypes = [ctypes.POINTER(attn_bwd_args)]
+        lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.attn_bwd_ex.argtypes = [ctypes.POINTER(attn_bwd_args)]
+        lib.attn_bwd_ex.restype = ctypes.c_int
+        lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I32, I32, P, I64,
+                                 I32, P, ctypes.c_size_t, P]
+        lib.attn_bwd.restype = ctypes.c_int
+        lib.attn_bwd_delta.argtypes = [P, P, P, I64, I64, I64, I64, I32, P]
+        lib.attn_bwd_delta.restype = ctypes.c_int
+        lib.attn_bwd_strerror.argtypes = [ctypes.c_int]
+        lib.attn_bwd_strerror.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def attn_bwd_strerror(status: int) -> str:
+    return load().attn_bwd_strerror(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != ATTN_OK:
+        raise AttnBwdError(status, attn_bwd_strerror(status))
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_args(q, k, v, o, dout, lse, dq, dk, dv, *, scale, causal=True, window=0, topk_idx=None,
+              workspace=None, stream=None) -> attn_bwd_args:
+    """Fill an attn_bwd_args from torch tensors (shapes taken from q [B,Sq,Hq,Dqk], k, v)."""
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    dt = q.dtype
+    B, Sq, Hq, Dqk = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    Dv = v.shape[3]
+    a = attn_bwd_args()
+    a.q, a.k, a.v = _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt)
+    a.o, a.dout = _dev(o, "o", dt), _dev(dout, "dout", dt)
+    a.lse = _dev(lse, "lse", torch.float32)
+    a.topk_idx = _dev(topk_idx, "topk_idx", torch.int32)
+    a.dq, a.dk, a.dv = _dev(dq, "dq", dt), _dev(dk, "dk", dt), _dev(dv, "dv", dt)
+    a.B, a.Sq, a.Skv, a.Hq, a.Hkv, a.Dqk, a.Dv = B, Sq, Skv, Hq, Hkv, Dqk, Dv
+    a.topk = 0 if topk_idx is None else topk_idx.shape[-1]
+    a.scale = float(scale)
+    a.causal = int(bool(causal))
+    a.window = int(window)
+    a.dtype = _DT[dt]
+    if workspace is not None:
+        a.workspace = _dev(workspace, "workspace")
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.stream = _stream(stream)
+    return a
+
+
+def attn_bwd_workspace_size(args: attn_bwd_args) -> int:
+    return int(load().attn_bwd_workspace_size(ctypes.byref(args)))
+
+
+def attn_bwd_ex(args: attn_bwd_args) -> None:
+    _check(load().attn_bwd_ex(ctypes.byref(args)))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, S, Hq, Hkv, D, scale, causal, window, topk_idx=None, topk=0,
+             dtype=None, workspace=None, workspace_bytes=0, stream=None) -> None:
+    """The spec ordered entry point (Sq = Skv = S, Dqk = Dv = D), tensors or raw pointers."""
+    ptr = lambda t: t.data_ptr() if isinstance(t, torch.Tensor) else t  # noqa: E731
+    if dtype is None:
+        dtype = _DT[q.dtype]
+    if isinstance(workspace, torch.Tensor):
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(load().attn_bwd(ptr(q), ptr(k), ptr(v), ptr(o), ptr(dout), ptr(lse), ptr(dq), ptr(dk), ptr(dv), B, S, Hq,
+                           Hkv, D, float(scale), int(causal), int(window), ptr(topk_idx), int(topk), int(dtype),
+                           ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def attn_bwd_delta(o, dout, delta, stream=None) -> None:
+    """delta [B,Hq,Sq] f32 = rowsum(o * dout) for o, dout [B,Sq,Hq,Dv] (the preprocess alone)."""
+    B, Sq, Hq, Dv = o.shape
+    dt = o.dtype
+    _check(load().attn_bwd_delta(_dev(o, "o", dt), _dev(dout, "dout", dt), _dev(delta, "delta", torch.float32), B, Sq,
+                                 Hq, Dv, _DT[dt], _stream(stream)))

@@ -1,0 +1,187 @@
+// api.hip -- the extern "C" boundary of libattn_bwd.so (declared in include/attn_bwd.h).
+//
+// Validates every argument on the host before anything is enqueued, carves the workspace,
+// and enqueues the kernels on the caller's stream:
+//   dense:  delta (preprocess) -> dK/dV (KV-block owned) -> dQ (query-block owned)
+//   top-k:  not built yet (ATTN_E_UNSUPPORTED).
+// The library keeps no state between calls.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "attn_bwd.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_msg[512];
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+int set_hip_error(hipError_t e, const char *what) {
+  snprintf(g_msg, sizeof(g_msg), "HIP error in %s: %s", what, hipGetErrorString(e));
+  return ATTN_E_HIP;
+}
+
+// Structural validation (no pointers dereferenced, no HIP calls).
+int validate_sizes(const attn_bwd_args *a) {
+  if (!a) return ATTN_E_INVAL;
+  if (a->B < 1 || a->Sq < 1 || a->Skv < 1 || a->Hq < 1 || a->Hkv < 1 || a->Dqk < 1 || a->Dv < 1) return ATTN_E_INVAL;
+  if (a->Hq % a->Hkv != 0) return ATTN_E_INVAL;
+  if (a->causal != 0 && a->causal != 1) return ATTN_E_INVAL;
+  if (a->window < 0) return ATTN_E_INVAL;
+  if (a->window > 0 && (!a->causal || a->topk_idx)) return ATTN_E_INVAL;
+  if (a->topk_idx && a->topk < 1) return ATTN_E_INVAL;
+  if (!a->topk_idx && a->topk != 0) return ATTN_E_INVAL;
+  if (!(a->scale > 0.f) || !isfinite(a->scale)) return ATTN_E_INVAL;
+  if (a->dtype != ATTN_DT_F16 && a->dtype != ATTN_DT_BF16) return ATTN_E_INVAL;
+  // 32-bit row indices inside the kernels: every row count must fit comfortably.
+  const int64_t lim = (int64_t)1 << 31;
+  if (a->B * a->Sq * a->Hq >= lim || a->B * a->Skv * a->Hkv >= lim) return ATTN_E_UNSUPPORTED;
+  if (a->topk_idx) return ATTN_E_UNSUPPORTED;  // the gathered top-k kernels are not built yet
+  if (!((a->Dqk == 64 && a->Dv == 64) || (a->Dqk == 128 && a->Dv == 128))) return ATTN_E_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+size_t workspace_bytes_for(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Hq * a->Sq) * sizeof(float)); }
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_workspace_size(const attn_bwd_args *a) {
+  if (validate_sizes(a) != ATTN_OK) return 0;
+  return workspace_bytes_for(a);
+}
+
+int attn_bwd_ex(const attn_bwd_args *a) {
+  int rc = validate_sizes(a);
+  if (rc != ATTN_OK) return rc;
+  const void *ptrs[] = {a->q, a->k, a->v, a->o, a->dout, a->lse, a->dq, a->dk, a->dv};
+  for (const void *p : ptrs)
+    if (!p || !aligned16(p)) return ATTN_E_INVAL;
+  const size_t need = workspace_bytes_for(a);
+  if (a->workspace) {
+    if (((uintptr_t)a->workspace & 255) != 0) return ATTN_E_INVAL;
+    if (a->workspace_bytes < need) return ATTN_E_WORKSPACE;
+  } else if (a->workspace_bytes != 0) {
+    return ATTN_E_INVAL;
+  }
+
+  hipStream_t st = (hipStream_t)a->stream;
+  const bool bf16 = a->dtype == ATTN_DT_BF16;
+  void *ws = a->workspace;
+  if (!ws) {
+    hipError_t e = hipMallocAsync(&ws, need, st);
+    if (e != hipSuccess) return set_hip_error(e, "hipMallocAsync(workspace)");
+  }
+
+  attn::Params p;
+  p.q = (const short *)a->q;
+  p.k = (const short *)a->k;
+  p.v = (const short *)a->v;
+  p.o = (const short *)a->o;
+  p.dout = (const short *)a->dout;
+  p.lse = a->lse;
+  p.delta = (float *)ws;
+  p.idx = a->topk_idx;
+  p.dq = (short *)a->dq;
+  p.dk = (short *)a->dk;
+  p.dv = (short *)a->dv;
+  p.B = (int)a->B;
+  p.Sq = (int)a->Sq;
+  p.Skv = (int)a->Skv;
+  p.Hq = (int)a->Hq;
+  p.Hkv = (int)a->Hkv;
+  p.G = (int)(a->Hq / a->Hkv);
+  p.topk = (int)a->topk;
+  p.Dqk = (int)a->Dqk;
+  p.Dv = (int)a->Dv;
+  p.causal = a->causal;
+  p.window = a->window;
+  p.scale = a->scale;
+  p.c = (float)((double)a->scale * 1.4426950408889634);
+
+  hipEvent_t *ev = (hipEvent_t *)a->events;
+  hipError_t e = ev ? hipEventRecord(ev[0], st) : hipSuccess;
+  if (e == hipSuccess) e = attn::launch_delta(p.o, p.dout, p.delta, a->B, a->Sq, a->Hq, a->Dv, bf16, st);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+  if (e == hipSuccess) e = attn::launch_dense_dkdv(p, bf16, st);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+  if (e == hipSuccess) e = attn::launch_dense_dq(p, bf16, st);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
+  if (!a->workspace) {
+    hipError_t e2 = hipFreeAsync(ws, st);
+    if (e == hipSuccess && e2 != hipSuccess) return set_hip_error(e2, "hipFreeAsync(workspace)");
+  }
+  if (e != hipSuccess) return set_hip_error(e, "kernel launch");
+  return ATTN_OK;
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse, void *dq,
+             void *dk, void *dv, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, float scale, int32_t causal,
+             int32_t window, const int32_t *topk_idx, int64_t topk, int32_t dtype, void *workspace,
+             size_t workspace_bytes, void *stream) {
+  attn_bwd_args a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.topk_idx = topk_idx;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.Sq = S;
+  a.Skv = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Dqk = D;
+  a.Dv = D;
+  a.topk = topk;
+  a.scale = scale;
+  a.causal = causal;
+  a.window = window;
+  a.dtype = dtype;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  a.stream = stream;
+  return attn_bwd_ex(&a);
+}
+
+int attn_bwd_delta(const void *o, const void *dout, float *delta, int64_t B, int64_t Sq, int64_t Hq, int64_t Dv,
+                   int32_t dtype, void *stream) {
+  if (!o || !dout || !delta || !aligned16(o) || !aligned16(dout) || !aligned16(delta)) return ATTN_E_INVAL;
+  if (B < 1 || Sq < 1 || Hq < 1) return ATTN_E_INVAL;
+  if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16) return ATTN_E_INVAL;
+  if (Dv != 64 && Dv != 128 && Dv != 256 && Dv != 512) return ATTN_E_UNSUPPORTED;
+  hipError_t e = attn::launch_delta((const short *)o, (const short *)dout, delta, B, Sq, Hq, Dv, dtype == ATTN_DT_BF16,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return set_hip_error(e, "delta launch");
+  return ATTN_OK;
+}
+
+const char *attn_bwd_strerror(int status) {
+  switch (status) {
+    case ATTN_OK:
+      return "success";
+    case ATTN_E_INVAL:
+      return "invalid argument (null or misaligned pointer, bad size, Hq % Hkv != 0, bad flag combination)";
+    case ATTN_E_UNSUPPORTED:
+      return "unsupported: no kernel for this head-dim / variant in this build";
+    case ATTN_E_WORKSPACE:
+      return "workspace smaller than attn_bwd_workspace_size()";
+    case ATTN_E_HIP:
+      return g_msg[0] ? g_msg : "HIP runtime error";
+    default:
+      return "unknown status";
+  }
+}
+
+}  // extern "C"

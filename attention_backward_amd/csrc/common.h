@@ -1,0 +1,79 @@
+// common.h -- device-side types and helpers shared by the attention-backward kernels (gfx950).
+//
+// MFMA operand layouts used throughout (v_mfma_f32_32x32x16_{f16,bf16}, wave64), measured on
+// MI355X with an in-bounds probe:
+//   A (32 x 16, M x K):  lane l holds A[m = l % 32][k = 8*(l/32) + e], e = 0..7
+//   B (16 x 32, K x N):  lane l holds B[k = 8*(l/32) + e][n = l % 32]
+//   C (32 x 32, f32):    lane l, register r holds C[m = 8*(r/4) + 4*(l/32) + r%4][n = l % 32]
+// Because a contraction may use any order of its k index as long as A and B agree, the C block
+// of one product can feed the next product directly: the 8 registers 8s..8s+7 of a lane cover
+// the 16 rows m in {16s + 8*(e/4) + 4*(l/32) + e%4}, i.e. a permutation of 16s..16s+15.  The
+// matching operand is read with ds_read_tr16_b64 (gfx950), which, within each group of 16
+// lanes, takes four 16-element rows supplied by lanes 4r..4r+3 and hands lane i column i of
+// those four rows -- two such reads give exactly the 8 permuted k values a lane needs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef short s8v __attribute__((ext_vector_type(8)));    // 8 x 16-bit: one MFMA A or B operand
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));  // one 32x32 f32 accumulator block
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef __bf16 b8v __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Params {
+  const short *q, *k, *v, *o, *dout;  // element bits of fp16/bf16
+  const float *lse;                   // [B,Hq,Sq] base 2
+  float *delta;                       // [B,Hq,Sq] workspace
+  const int32_t *idx;                 // [B,Sq,Hkv,topk] or null
+  short *dq, *dk, *dv;
+  int B, Sq, Skv, Hq, Hkv, G, topk, Dqk, Dv;
+  int causal, window;
+  float scale;                        // softmax scale
+  float c;                            // scale * log2(e)
+};
+
+// SPLIT: whether P and dS enter their MFMA products (dV += P^T dO, dK += dS^T Q, dQ += dS K) as
+// hi + lo halves.  bf16 keeps 8 mantissa bits, so one rounding costs up to 2^-9 relative per
+// term; over the long sums of dK, dQ and dV that exceeds the 5e-3 / 1e-2 tolerance against the
+// f64 oracle (measured), while hi = bf16(x), lo = bf16(x - hi) carries 16 bits.  fp16's 11 bits
+// need no split.
+struct F16 {
+  static constexpr bool SPLIT = false;
+  static __device__ __forceinline__ f16v mfma(s8v a, s8v b, f16v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8v, a), __builtin_bit_cast(h8v, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ short cvt(float x) { return __builtin_bit_cast(short, (_Float16)x); }
+  static __device__ __forceinline__ float tof(short x) { return (float)__builtin_bit_cast(_Float16, x); }
+};
+
+struct BF16 {
+  static constexpr bool SPLIT = true;
+  static __device__ __forceinline__ f16v mfma(s8v a, s8v b, f16v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8v, a), __builtin_bit_cast(b8v, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ short cvt(float x) { return __builtin_bit_cast(short, (__bf16)x); }
+  static __device__ __forceinline__ float tof(short x) {
+    return __builtin_bit_cast(float, ((unsigned)(unsigned short)x) << 16);
+  }
+};
+
+__device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Transposed LDS read of four 16-bit values (see the header comment).
+__device__ __forceinline__ s4v lds_tr4(const short *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v *)(p));
+}
+
+__device__ __forceinline__ s8v cat8(s4v a, s4v b) { return s8v{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
+
+// lse as the kernels use it: a row with lse = -inf (no allowed key) must give p = 0, so it is
+// mapped to +inf; exp2(x - inf) = 0.
+__device__ __forceinline__ float lse_fix(float l) { return l == -__builtin_inff() ? __builtin_inff() : l; }
+
+}  // namespace attn

@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention backward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one whole backward call (preprocess + dK/dV kernel + dQ kernel) on inputs already
+resident in HBM.  The default workload is the 2x2048x32x128 fp16 causal MHA backward.
+Prints one JSON line: causal-adjusted TFLOP/s (2.5 x forward flops over the exact unmasked
+pairs), its fraction of the 2.5 PFLOP/s dense fp16/bf16 MFMA peak, per-kernel times from HIP
+events recorded on the launch stream, the dominant kernel's roofline, a cold-cache per-call
+median, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from attention_backward_amd import synth  # noqa: E402
+
+PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16
+PEAK_HBM_GBS = 8000.0
+LOG2E = 1.4426950408889634
+METRIC = "attn-bwd TFLOP/s (causal-adjusted) + % of MI355X fp16/bf16 MFMA peak"
+
+
+def pairs(w) -> int:
+    off = w.Skv - w.Sq
+    if w.topk:
+        return w.B * w.Hq * w.Sq * w.topk
+    i = np.arange(w.Sq, dtype=np.int64)
+    hi = np.minimum(w.Skv - 1, i + off) if w.causal else np.full_like(i, w.Skv - 1)
+    lo = np.maximum(0, i + off - w.window + 1) if w.window > 0 else np.zeros_like(i)
+    return int(np.maximum(0, hi - lo + 1).sum()) * w.B * w.Hq
+
+
+def gpu_forward_inputs(q, k, v, w):
+    """Input preparation (not timed): O in the storage dtype and base-2 lse in f32 of the masked
+    softmax forward over the drawn inputs, evaluated with torch fp32 matmuls on the GPU."""
+    B, Sq, Hq, _ = q.shape
+    Skv, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    G = Hq // Hkv
+    off = Skv - Sq
+    c = w.scale * LOG2E
+    o = torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    rows = 1024
+    for b in range(B):
+        for h in range(Hq):
+            kk = k[b, :, h // G].float()
+            kt = kk.t().contiguous()
+            vv = v[b, :, h // G].float().contiguous()
+            qq = q[b, :, h].float()
+            for i0 in range(0, Sq, rows):
+                i1 = min(Sq, i0 + rows)
+                s = (qq[i0:i1] @ kt) * c
+                ii = torch.arange(i0, i1, device=q.device).unsqueeze(1)
+                jj = torch.arange(Skv, device=q.device).unsqueeze(0)
+                ok = torch.ones_like(s, dtype=torch.bool)
+                if w.causal:
+                    ok &= jj <= ii + off
+                if w.window > 0:
+                    ok &= jj > ii + off - w.window
+                s = torch.where(ok, s, torch.full_like(s, -math.inf))
+                m = s.amax(1, keepdim=True)
+                empty = torch.isinf(m) & (m < 0)
+                m = torch.where(empty, torch.zeros_like(m), m)
+                p = torch.exp2(s - m)
+                tot = p.sum(1, keepdim=True)
+                safe = torch.where(empty, torch.ones_like(tot), tot)
+                o[b, i0:i1, h] = torch.where(empty, torch.zeros_like(tot), (p @ vv) / safe).to(q.dtype)
+                lse[b, h, i0:i1] = torch.where(empty, torch.full_like(m, -math.inf), m + torch.log2(safe)).squeeze(1)
+    return o, lse
+
+
+def cpu_baseline(w, inp_cpu, target_s):
+    """The f64 CPU oracle, as it stands, on a bounded sample of the workload: the full backward of
+    the first n heads of batch 0 (n chosen so the run takes about target_s seconds)."""
+    import oracle  # the oracle is test infrastructure; this leg only times it
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+
+    def run(nh):
+        G = w.G
+        nkv = max(1, nh // G)
+        nh = nkv * G
+        sl = lambda t, n: t[:1, :, :n].contiguous()  # noqa: E731
+        args = (sl(inp_cpu["q"], nh), sl(inp_cpu["k"], nkv), sl(inp_cpu["v"], nkv), sl(inp_cpu["o"], nh),
+                sl(inp_cpu["dout"], nh), inp_cpu["lse"][:1, :nh].contiguous())
+        t0 = time.perf_counter()
+        oracle.bwd(*args, w.scale, w.causal, w.window)
+        return time.perf_counter() - t0, nh
+
+    dt1, nh1 = run(w.G)
+    nh = min(w.Hq, max(nh1, int(nh1 * target_s / max(dt1, 1e-3))))
+    dt, nh = run(nh) if nh > nh1 else (dt1, nh1)
+    sample = w.with_(B=1, Hq=nh, Hkv=max(1, nh // w.G))
+    flops = 2.5 * pairs(sample) * (2 * w.Dqk + 2 * w.Dv)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"full f64 backward of batch 0, query heads 0..{nh - 1} of {w.Hq} ({nh}/{w.B * w.Hq} of the "
+                      f"workload's heads), {dt:.1f} s", "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cold-iters", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this backward needs no inter-GPU communication; "
+              "run it with --gpus 1 (see the sharding note in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import attention_backward_amd as ab
+
+    w = synth.WORKLOADS[args.workload]
+    if w.topk:
+        print(f"{w.name}: the top-k kernels are not built yet", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(w)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+    o, lse = gpu_forward_inputs(q, k, v, w)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    a = ab.make_args(q, k, v, o, do, lse, dq, dk, dv, scale=w.scale, causal=w.causal, window=w.window)
+    need = ab.attn_bwd_workspace_size(a)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), need
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        ab.attn_bwd_ex(a)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K back-to-back steps, with 4 events per step recorded by the library
+    # on its launch stream around its three kernels.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    import ctypes
+
+    for row in ev:
+        for e in row:
+            e.record(stream)  # materialise the underlying hipEvent before taking its handle
+    torch.cuda.synchronize()
+    ev_arrays = [(ctypes.c_void_p * 4)(*[e.cuda_event for e in row]) for row in ev]
+    assert all(h for arr in ev_arrays for h in arr), "HIP event handles must be non-null"
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        a.events = ctypes.cast(ev_arrays[s], ctypes.c_void_p)
+        ab.attn_bwd_ex(a)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    a.events = None
+    per = {"delta": [], "dkdv": [], "dq": [], "call": []}
+    for row in ev:
+        per["delta"].append(row[0].elapsed_time(row[1]) * 1e3)
+        per["dkdv"].append(row[1].elapsed_time(row[2]) * 1e3)
+        per["dq"].append(row[2].elapsed_time(row[3]) * 1e3)
+        per["call"].append(row[0].elapsed_time(row[3]) * 1e3)
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Cold-cache per-call timing (the pages flush L2 before every iteration): a 1 GiB write
+    # before each call evicts the 256 MB Infinity Cache and the per-XCD L2s.
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(args.cold_iters):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ab.attn_bwd_ex(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+
+    npairs = pairs(w)
+    flops = 2.5 * npairs * (2 * w.Dqk + 2 * w.Dv)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    esz = 2
+    med = {kname: statistics.median(vals) for kname, vals in per.items()}
+    mean = {kname: statistics.fmean(vals) for kname, vals in per.items()}
+    dkdv_flops = npairs * (4 * w.Dqk + 4 * w.Dv)   # S, dP, dV, dK products
+    dq_flops = npairs * (4 * w.Dqk + 2 * w.Dv)     # S, dP recomputed, dQ
+    delta_bytes = 2 * w.B * w.Sq * w.Hq * w.Dv * esz + 4 * w.B * w.Hq * w.Sq
+    dkdv_tf = dkdv_flops / (mean["dkdv"] * 1e-6) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: N(0,1) q,k,v,dO from a seeded PCG64 generator; O and lse from an fp32 forward",
+        "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal, "window": w.window, "topk": w.topk,
+                   "metric_flops": flops, "pairs": npairs},
+        "roofline": {"kernel": "dense_dkdv", "bound": "mfma", "achieved": round(dkdv_tf, 2),
+                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(dkdv_tf / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": dkdv_flops},
+        "kernels_us_median": {kname: round(v_, 2) for kname, v_ in med.items()},
+        "kernels": {
+            "delta": {"us": round(mean["delta"], 2), "GB/s": round(delta_bytes / (mean["delta"] * 1e-6) / 1e9, 1),
+                      "frac_hbm": round(delta_bytes / (mean["delta"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+            "dkdv": {"us": round(mean["dkdv"], 2), "TFLOP/s": round(dkdv_tf, 1)},
+            "dq": {"us": round(mean["dq"], 2),
+                   "TFLOP/s": round(dq_flops / (mean["dq"] * 1e-6) / 1e12, 1)},
+        },
+        "cold_call_us": {"median": round(statistics.median(cold), 2), "min": round(min(cold), 2),
+                         "max": round(max(cold), 2), "n": len(cold),
+                         "tflops_at_median": round(flops / (statistics.median(cold) * 1e-6) / 1e12, 1)},
+    }
+    if not args.no_cpu_baseline:
+        inp_cpu = {n: inp[n] for n in ("q", "k", "v", "dout")}
+        inp_cpu["o"], inp_cpu["lse"] = o.cpu(), lse.cpu()
+        result["cpu_baseline"] = cpu_baseline(w, inp_cpu, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

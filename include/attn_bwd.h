@@ -1,0 +1,119 @@
+/*
+ * attn_bwd.h -- C ABI of libattn_bwd.so, the fused softmax-attention backward for AMD gfx950
+ * (MI355X).
+ *
+ * The operation (TileOPs PR #2281 page, "TileFoundry Description", the Reference program; MHA is
+ * the grouped-query op with Hkv = Hq, as the same page's summary says):
+ *
+ *   given q, k, v, the forward output o, its gradient dout and the forward's base-2 log-sum-exp
+ *   lse, compute for every batch b, query head h (KV head g = h / (Hq/Hkv)) and query row i
+ *     delta_i = sum_d o[i,d] * dout[i,d]
+ *     p_ij    = exp2(scale * log2(e) * (q_i . k_j) - lse_i)   for keys j allowed to row i, else 0
+ *     ds_ij   = p_ij * (dout_i . v_j - delta_i)
+ *     dq_i    = scale * sum_j ds_ij k_j
+ *     dk_j    = scale * sum_(h in g) sum_i ds_ij q_i      (summed over the G query heads of g)
+ *     dv_j    =         sum_(h in g) sum_i p_ij dout_i
+ *
+ * Allowed keys of query row i, with off = Skv - Sq (bottom-right alignment):
+ *   dense:   causal   => j <= i + off
+ *            window>0 => j >  i + off - window   (window = number of visible keys including the
+ *                                                 diagonal; flash-linear-attention issue #8,
+ *                                                 sliding-window GQA)
+ *   top-k:   the entries of topk_idx[b, i, g, 0..topk) (TileLang PR #2592, sparse MLA backward),
+ *            once per occurrence; entries < 0, >= Skv, or (causal) > i + off are ignored.
+ * A row with no allowed key, or with lse = -inf, contributes nothing.  Key rows that no query
+ * reaches get dk = dv = 0.  dk and dv are produced directly at Hkv heads, with no Hq-shaped
+ * intermediate (flash-linear-attention issue #8, KV-head-owned dK/dV).
+ *
+ * Layouts (row-major, contiguous, "BSHD"):
+ *   q    [B, Sq,  Hq,  Dqk]    k  [B, Skv, Hkv, Dqk]    v  [B, Skv, Hkv, Dv]
+ *   o    [B, Sq,  Hq,  Dv ]    dout like o              lse [B, Hq, Sq]  float32, base 2
+ *   dq like q, dk like k, dv like v; element type = dtype (fp16 or bf16) for all of them.
+ *   topk_idx [B, Sq, Hkv, topk] int32, or NULL for the dense path.
+ *
+ * Ownership and execution:
+ *   - every pointer is a DEVICE pointer owned by the caller; inputs are never written;
+ *   - all work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream);
+ *     the call never synchronises, results are ready once the caller synchronises the stream;
+ *   - every element of dq, dk and dv is written on every successful call;
+ *   - the library keeps no state between calls: calls with distinct outputs and workspaces are
+ *     independent and may run concurrently on different streams.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued.  On error nothing
+ * is enqueued, the outputs are untouched and a negative attn_status is returned;
+ * attn_bwd_strerror() describes it (for ATTN_E_HIP, with the HIP error string of the last
+ * failing call on this thread).
+ */
+#ifndef ATTN_BWD_H
+#define ATTN_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_DT_F16 = 0, ATTN_DT_BF16 = 1 } attn_dtype;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_INVAL = -1,        /* a null/misaligned pointer, a negative size, Hq % Hkv != 0, ... */
+  ATTN_E_UNSUPPORTED = -2,  /* a valid request this build has no kernel for (head dims, dtype) */
+  ATTN_E_WORKSPACE = -3,    /* workspace_bytes smaller than attn_bwd_workspace_size()         */
+  ATTN_E_HIP = -4           /* a HIP runtime call or kernel launch failed                      */
+} attn_status;
+
+/* Full argument set.  Sizes are int64; Sq != Skv and Dqk != Dv are allowed where a kernel
+ * exists: dense (Dqk, Dv) in {(64,64), (128,128)}; top-k (Dqk, Dv) = (576, 512). */
+typedef struct {
+  const void *q, *k, *v, *o, *dout; /* 16-byte aligned device pointers, element type = dtype   */
+  const float *lse;                 /* [B, Hq, Sq] float32, base-2 log-sum-exp of the forward   */
+  const int32_t *topk_idx;          /* NULL => dense; else [B, Sq, Hkv, topk] int32            */
+  void *dq, *dk, *dv;               /* outputs, 16-byte aligned, element type = dtype          */
+  int64_t B, Sq, Skv, Hq, Hkv, Dqk, Dv, topk;
+  float scale;                      /* softmax scale (finite, > 0), typically 1/sqrt(Dqk)      */
+  int32_t causal;                   /* 0 or 1                                                  */
+  int32_t window;                   /* 0 = no window; > 0 requires causal = 1 and no topk_idx  */
+  int32_t dtype;                    /* attn_dtype                                              */
+  void *workspace;                  /* device scratch of workspace_bytes, 256-byte aligned, or
+                                       NULL with workspace_bytes = 0: the library then takes
+                                       stream-ordered memory (hipMallocAsync/hipFreeAsync)     */
+  size_t workspace_bytes;
+  void *stream;                     /* hipStream_t                                             */
+  void *events;                     /* optional, NULL or an array of 4 hipEvent_t created by the
+                                       caller: recorded on `stream` before the preprocess,
+                                       after it, after the dK/dV kernel and after the dQ kernel
+                                       (per-kernel timing without changing the work)          */
+} attn_bwd_args;
+
+/* Bytes of workspace the call needs for these sizes (0 if the arguments are invalid).
+ * Dense: delta [B,Hq,Sq] f32.  Top-k: delta plus dK/dV f32 accumulators at Hkv heads.
+ * Never an Hq-shaped dK/dV buffer. */
+size_t attn_bwd_workspace_size(const attn_bwd_args *a);
+
+/* The backward for the full argument set.  Returns an attn_status. */
+int attn_bwd_ex(const attn_bwd_args *a);
+
+/* The same operation with Sq = Skv = S and Dqk = Dv = D, arguments in the order
+ *   q, k, v, o, dout, lse, dq, dk, dv, B, S, Hq, Hkv, D, scale, causal, window, topk_idx,
+ * followed by what the plain list cannot carry: topk, dtype, workspace, workspace_bytes, stream. */
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+             void *dq, void *dk, void *dv, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+             int32_t causal, int32_t window, const int32_t *topk_idx, int64_t topk, int32_t dtype, void *workspace,
+             size_t workspace_bytes, void *stream);
+
+/* Only the first step of the backward: delta [B,Hq,Sq] = rowsum(o * dout) in f32, enqueued on
+ * `stream`.  o and dout [B,Sq,Hq,Dv] with Dv in {64, 128, 256, 512}; delta 16-byte aligned. */
+int attn_bwd_delta(const void *o, const void *dout, float *delta, int64_t B, int64_t Sq, int64_t Hq, int64_t Dv,
+                   int32_t dtype, void *stream);
+
+/* Static description of a status code (never NULL).  For ATTN_E_HIP the string includes the
+ * HIP error text of the last failure on the calling thread. */
+const char *attn_bwd_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_BWD_H */

@@ -1,0 +1,96 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point include/attn_bwd.h declares,
+and rejects invalid arguments on the host (before any HIP call) with the documented status."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_backward_amd as ab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_bwd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = ab.load()
+    names = declared_functions()
+    assert set(names) == set(ab.EXPORTS), names
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def valid_args(**kw):
+    a = ab.attn_bwd_args()
+    fake = 0x100000  # aligned, never dereferenced: every case below fails validation first
+    for f in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"):
+        setattr(a, f, fake)
+    a.B, a.Sq, a.Skv, a.Hq, a.Hkv, a.Dqk, a.Dv, a.topk = 2, 2048, 2048, 32, 32, 128, 128, 0
+    a.scale, a.causal, a.window, a.dtype = 0.088, 1, 0, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_workspace_size():
+    assert ab.attn_bwd_workspace_size(valid_args()) == 2 * 32 * 2048 * 4
+    # never Hq-shaped dK/dV: GQA needs the same delta-only workspace
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=4)) == 2 * 32 * 2048 * 4
+    assert ab.attn_bwd_workspace_size(valid_args(B=1, Sq=3, Hq=2, Hkv=2)) == 256  # 256-byte granularity
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=5)) == 0
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=0), -1),
+        (dict(dk=0x100008), -1),          # misaligned output
+        (dict(lse=0x100004), -1),
+        (dict(B=0), -1),
+        (dict(Sq=-1), -1),
+        (dict(Hq=32, Hkv=5), -1),         # Hq % Hkv != 0
+        (dict(causal=2), -1),
+        (dict(window=-3), -1),
+        (dict(window=16, causal=0), -1),  # a window needs the causal mask
+        (dict(scale=0.0), -1),
+        (dict(scale=float("inf")), -1),
+        (dict(dtype=7), -1),
+        (dict(topk=4), -1),               # topk without an index list
+        (dict(Dqk=96, Dv=96), -2),        # no kernel for this head dim
+        (dict(Dqk=128, Dv=64), -2),
+        (dict(topk_idx=0x100000, topk=8), -2),  # top-k kernels not built yet
+        (dict(workspace=0x100000, workspace_bytes=16), -3),
+        (dict(workspace=0x100080, workspace_bytes=1 << 30), -1),  # workspace not 256-byte aligned
+        (dict(workspace=0, workspace_bytes=64), -1),
+    ],
+)
+def test_validation_statuses(kw, status):
+    a = valid_args(**kw)
+    rc = ab.load().attn_bwd_ex(ctypes.byref(a))
+    assert rc == status, (kw, rc, ab.attn_bwd_strerror(rc))
+    assert ab.attn_bwd_strerror(rc)
+
+
+def test_north_star_entry_point_validates():
+    lib = ab.load()
+    rc = lib.attn_bwd(None, None, None, None, None, None, None, None, None, 1, 128, 2, 2, 128, 0.1, 1, 0, None, 0, 0,
+                      None, 0, None)
+    assert rc == -1
+    rc = lib.attn_bwd_delta(None, None, None, 1, 1, 1, 128, 0, None)
+    assert rc == -1
+    rc = lib.attn_bwd_delta(0x1000, 0x1000, 0x1000, 1, 1, 1, 96, 0, None)
+    assert rc == -2
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 4, 1, 128, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        ab.make_args(q, q, q, q, q, torch.zeros(1, 1, 4), q, q, q, scale=0.1)

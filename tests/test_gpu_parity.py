@@ -1,0 +1,161 @@
+"""Parity of the HIP path (through the C ABI) with the f64 CPU oracle on the same seeded inputs.
+
+Small shapes are compared element by element over every output; they span several tiles of
+both kernels and have ragged tails.  The pages' full-size workloads run in exactly the launch
+configuration the benchmark times and are compared on sampled rows that the oracle computes
+one by one (its dq of a query row, its dk/dv of a key row).  Tolerance (fp16/bf16 outputs):
+|gpu - ref| <= 5e-3 + 1e-2 |ref| elementwise, the allclose the TileOPs page checks with.
+Outputs and workspace are NaN-poisoned before every call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_backward_amd as ab
+import oracle
+from attention_backward_amd import synth
+from tests.helpers import check_close, log, poisoned_like, prepare, sample_rows, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def run(inp, w):
+    g = to_gpu(inp)
+    dq, dk, dv = poisoned_like(g["q"]), poisoned_like(g["k"]), poisoned_like(g["v"])
+    args = ab.make_args(g["q"], g["k"], g["v"], g["o"], g["dout"], g["lse"], dq, dk, dv, scale=w.scale,
+                        causal=w.causal, window=w.window, topk_idx=g["idx"])
+    need = ab.attn_bwd_workspace_size(args)
+    assert need > 0
+    ws = poisoned_like(torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda"))
+    args.workspace, args.workspace_bytes = ws.data_ptr(), need
+    ab.attn_bwd_ex(args)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def full_compare(w, inp=None):
+    log(f"case {w.name}: B={w.B} Sq={w.Sq} Skv={w.Skv} Hq={w.Hq} Hkv={w.Hkv} D={w.Dqk}/{w.Dv} {w.dtype} "
+        f"causal={w.causal} window={w.window}")
+    inp = inp or prepare(w)
+    dq, dk, dv = run(inp, w)
+    ref = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["o"], inp["dout"], inp["lse"], w.scale, w.causal, w.window)
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        check_close(name, got.double().numpy(), r)
+    return inp, (dq, dk, dv)
+
+
+def small(name, **kw):
+    base = dict(B=1, Sq=256, Skv=256, Hq=2, Hkv=2, Dqk=128, Dv=128, dtype="fp16", causal=True, window=0, topk=0,
+                seed=100)
+    base.update(kw)
+    return synth.Workload(name=name, **base)
+
+
+SMALL = [
+    W["mha_causal_b1_s256_h2_d128_fp16"],
+    small("gqa_g4_bf16_ragged", B=2, Sq=300, Skv=300, Hq=8, Hkv=2, dtype="bf16", seed=101),
+    small("swa_d64_ragged", B=2, Sq=600, Skv=600, Hq=4, Hkv=2, Dqk=64, Dv=64, window=100, seed=102),
+    small("full_noncausal_d64_bf16", Sq=200, Skv=200, Hq=2, Hkv=1, Dqk=64, Dv=64, dtype="bf16", causal=False,
+          seed=103),
+    small("causal_sq_lt_skv", Sq=200, Skv=328, Hq=4, Hkv=4, seed=104),
+    small("causal_sq_gt_skv_empty_rows", Sq=300, Skv=130, Hq=2, Hkv=1, seed=105),
+    small("swa_g8_d128_window37", B=1, Sq=333, Skv=333, Hq=8, Hkv=1, window=37, seed=106),
+    small("swa_window1024_t2500", B=1, Sq=2500, Skv=2500, Hq=4, Hkv=2, Dqk=64, Dv=64, window=1024, seed=107),
+    small("mha_causal_s1024_h4_bf16", Sq=1024, Skv=1024, Hq=4, Hkv=4, dtype="bf16", seed=108),
+] + [small(f"tiny_s{s}", Sq=s, Skv=s, seed=110 + s) for s in (1, 2, 63, 65, 127, 129)]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_full_parity(w):
+    full_compare(w)
+
+
+def test_deterministic_and_both_entry_points():
+    w = SMALL[1]
+    inp = prepare(w)
+    a = run(inp, w)
+    b = run(inp, w)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16)), "outputs differ between two identical calls"
+    # the spec ordered entry point gives the same bits
+    g = to_gpu(inp)
+    dq, dk, dv = poisoned_like(g["q"]), poisoned_like(g["k"]), poisoned_like(g["v"])
+    ab.attn_bwd(g["q"], g["k"], g["v"], g["o"], g["dout"], g["lse"], dq, dk, dv, w.B, w.Sq, w.Hq, w.Hkv, w.Dqk,
+                w.scale, w.causal, w.window)
+    torch.cuda.synchronize()
+    for x, y in zip(a, (dq.cpu(), dk.cpu(), dv.cpu())):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype,Dv", [("fp16", 128), ("bf16", 64), ("bf16", 512), ("fp16", 256)])
+def test_delta_preprocess(dtype, Dv):
+    r = np.random.default_rng(Dv)
+    B, Sq, Hq = 2, 333, 3
+    o = synth.round_to(r.standard_normal((B, Sq, Hq, Dv), dtype=np.float32), dtype)
+    do = synth.round_to(r.standard_normal((B, Sq, Hq, Dv), dtype=np.float32), dtype)
+    delta = poisoned_like(torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda"))
+    ab.attn_bwd_delta(o.cuda(), do.cuda(), delta)
+    torch.cuda.synchronize()
+    ref = oracle.delta(o, do)
+    bound = 1e-6 + 1e-5 * np.einsum("bihd->bhi", np.abs(o.double().numpy() * do.double().numpy()))
+    err = np.abs(delta.cpu().double().numpy() - ref)
+    log(f"  delta {dtype} Dv={Dv}: max err {err.max():.3e}")
+    assert np.all(err <= bound)
+
+
+def test_masked_keys_do_not_matter():
+    """Changing K/V rows that no query can see changes no output bit (Sq < Skv, window)."""
+    w = small("masked_keys", Sq=128, Skv=1024, Hq=2, Hkv=1, window=200, seed=120)
+    inp = prepare(w)
+    a = run(inp, w)
+    inp2 = dict(inp)
+    k2, v2 = inp["k"].clone(), inp["v"].clone()
+    # query i sees keys (i + 896 - 200, i + 896]: keys < 697 are never visible
+    k2[:, :697] = 3.0
+    v2[:, :697] = -3.0
+    inp2["k"], inp2["v"] = k2, v2
+    b = run(inp2, w)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    assert torch.all(a[1][:, :697] == 0) and torch.all(a[2][:, :697] == 0)
+
+
+FULL = ["mha_causal_b2_s2048_h32_d128_fp16", "gqa_causal_b1_t16384_hq32_hkv4_d128_bf16",
+        "swa_gqa_b2_t8192_hq16_hkv8_d64_w1024_fp16", "swa_gqa_b2_t8000_hq16_hkv8_d64_w1024_fp16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name):
+    w = W[name]
+    log(f"case {name} (full size, sampled rows)")
+    inp = prepare(w)
+    dq, dk, dv = run(inp, w)
+    rng = np.random.default_rng(7)
+    qrows = sample_rows(rng, 48, w.B, w.Sq, w.Hq)
+    krows = sample_rows(rng, 48, w.B, w.Skv, w.Hkv)
+    args = (inp["q"], inp["k"], inp["v"], inp["o"], inp["dout"], inp["lse"], w.scale)
+    ref_dq = oracle.bwd_dq_rows(*args, qrows, w.causal, w.window)
+    ref_dk, ref_dv = oracle.bwd_dkv_rows(*args, krows, w.causal, w.window)
+    got_dq = dq[qrows[:, 0], qrows[:, 1], qrows[:, 2]].double().numpy()
+    got_dk = dk[krows[:, 0], krows[:, 1], krows[:, 2]].double().numpy()
+    got_dv = dv[krows[:, 0], krows[:, 1], krows[:, 2]].double().numpy()
+    check_close("dq rows", got_dq, ref_dq)
+    check_close("dk rows", got_dk, ref_dk)
+    check_close("dv rows", got_dv, ref_dv)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+
+
+def test_topk_variant_reports_unsupported_until_built():
+    w = W["sparse_mla_b1_sq4096_skv8192_h64_dqk576_dv512_top2048_bf16"].with_(Sq=64, Skv=128, topk=16, Hq=64)
+    inp = synth.make_inputs(w)
+    g = {k: v.cuda() for k, v in inp.items() if v is not None}
+    o = torch.zeros_like(g["dout"])
+    lse = torch.zeros((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
+    args = ab.make_args(g["q"], g["k"], g["v"], o, g["dout"], lse, dq, dk, dv, scale=w.scale, topk_idx=g["idx"])
+    with pytest.raises(ab.AttnBwdError) as e:
+        ab.attn_bwd_ex(args)
+    assert e.value.status == -2
