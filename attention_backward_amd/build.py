@@ -30,6 +30,9 @@ CFLAGS = [
     "-fPIC",
     "-munsafe-fp-atomics",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results and accumulators in VGPRs: the kernels are laid out to fit 256 VGPRs per
+    # wave, and AGPR-form accumulators made the register allocator shuttle them every step.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

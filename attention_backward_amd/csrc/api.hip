@@ -46,7 +46,9 @@ int validate_sizes(const attn_bwd_args *a) {
   return ATTN_OK;
 }
 
-size_t workspace_bytes_for(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Hq * a->Sq) * sizeof(float)); }
+// Workspace: delta [B,Hq,Sq] f32, then the sanitised lse [B,Hq,Sq] f32, each 256-byte aligned.
+size_t row_stat_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Hq * a->Sq) * sizeof(float)); }
+size_t workspace_bytes_for(const attn_bwd_args *a) { return 2 * row_stat_bytes(a); }
 
 }  // namespace
 
@@ -85,8 +87,8 @@ int attn_bwd_ex(const attn_bwd_args *a) {
   p.v = (const short *)a->v;
   p.o = (const short *)a->o;
   p.dout = (const short *)a->dout;
-  p.lse = a->lse;
   p.delta = (float *)ws;
+  p.lse = (const float *)((char *)ws + row_stat_bytes(a));
   p.idx = a->topk_idx;
   p.dq = (short *)a->dq;
   p.dk = (short *)a->dk;
@@ -107,7 +109,8 @@ int attn_bwd_ex(const attn_bwd_args *a) {
 
   hipEvent_t *ev = (hipEvent_t *)a->events;
   hipError_t e = ev ? hipEventRecord(ev[0], st) : hipSuccess;
-  if (e == hipSuccess) e = attn::launch_delta(p.o, p.dout, p.delta, a->B, a->Sq, a->Hq, a->Dv, bf16, st);
+  if (e == hipSuccess)
+    e = attn::launch_delta(p.o, p.dout, p.delta, a->lse, (float *)p.lse, a->B, a->Sq, a->Hq, a->Dv, bf16, st);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
   if (e == hipSuccess) e = attn::launch_dense_dkdv(p, bf16, st);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
@@ -161,8 +164,8 @@ int attn_bwd_delta(const void *o, const void *dout, float *delta, int64_t B, int
   if (B < 1 || Sq < 1 || Hq < 1) return ATTN_E_INVAL;
   if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16) return ATTN_E_INVAL;
   if (Dv != 64 && Dv != 128 && Dv != 256 && Dv != 512) return ATTN_E_UNSUPPORTED;
-  hipError_t e = attn::launch_delta((const short *)o, (const short *)dout, delta, B, Sq, Hq, Dv, dtype == ATTN_DT_BF16,
-                                    (hipStream_t)stream);
+  hipError_t e = attn::launch_delta((const short *)o, (const short *)dout, delta, nullptr, nullptr, B, Sq, Hq, Dv,
+                                    dtype == ATTN_DT_BF16, (hipStream_t)stream);
   if (e != hipSuccess) return set_hip_error(e, "delta launch");
   return ATTN_OK;
 }

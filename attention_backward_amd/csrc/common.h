@@ -28,7 +28,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct Params {
   const short *q, *k, *v, *o, *dout;  // element bits of fp16/bf16
-  const float *lse;                   // [B,Hq,Sq] base 2
+  const float *lse;                   // [B,Hq,Sq] base 2, -inf mapped to +inf (workspace copy)
   float *delta;                       // [B,Hq,Sq] workspace
   const int32_t *idx;                 // [B,Sq,Hkv,topk] or null
   short *dq, *dk, *dv;
@@ -71,6 +71,25 @@ __device__ __forceinline__ s4v lds_tr4(const short *p) {
 }
 
 __device__ __forceinline__ s8v cat8(s4v a, s4v b) { return s8v{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
+
+// LDS tiles are stored without row padding; the 16-byte chunk c of row R sits at chunk
+// c ^ swz(R).  swz takes 8 distinct values over any 8 aligned rows (so a ds_read_b128 of one
+// chunk across rows R..R+7 touches 8 distinct chunks = all banks once) and 4 distinct values
+// of swz/2 over any 4 aligned rows (so a transposed read of 32 bytes from each of rows
+// R..R+3 touches 4 distinct 32-byte slots).
+__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+
+// Asynchronous 16-byte copy global -> LDS: lane l of the wave writes lds_base + 16*l.
+// lds_base must be wave-uniform.  Completion is tracked by vmcnt (wait_vm0 below).
+__device__ __forceinline__ void g2lds16(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                   (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                   (__attribute__((address_space(3))) void *)lds_base, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // lse as the kernels use it: a row with lse = -inf (no allowed key) must give p = 0, so it is
 // mapped to +inf; exp2(x - inf) = 0.

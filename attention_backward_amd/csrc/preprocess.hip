@@ -11,9 +11,13 @@
 
 namespace attn {
 
+// Also copies lse (when lse_in is not null) into the workspace with -inf replaced by +inf: a row
+// whose lse is -inf has no allowed key and must contribute nothing, and exp2(x - inf) = 0
+// gives exactly that without a per-element test in the main kernels.
 template <class TT, int DV>
 __global__ __launch_bounds__(256) void delta_kernel(const short *__restrict__ o, const short *__restrict__ dout,
-                                                    float *__restrict__ delta, int64_t rows, int Sq, int Hq) {
+                                                    float *__restrict__ delta, const float *__restrict__ lse_in,
+                                                    float *__restrict__ lse_out, int64_t rows, int Sq, int Hq) {
   constexpr int TPR = DV / 8;       // lanes per row (16 bytes each)
   constexpr int RPB = 256 / TPR;    // rows per block per iteration
   const int sub = threadIdx.x % TPR;
@@ -29,30 +33,32 @@ __global__ __launch_bounds__(256) void delta_kernel(const short *__restrict__ o,
       const int64_t h = row % Hq;
       const int64_t i = (row / Hq) % Sq;
       const int64_t b = row / ((int64_t)Hq * Sq);
-      delta[(b * Hq + h) * Sq + i] = acc;
+      const int64_t x = (b * Hq + h) * Sq + i;
+      delta[x] = acc;
+      if (lse_in) lse_out[x] = lse_fix(lse_in[x]);
     }
   }
 }
 
 template <class TT, int DV>
-static hipError_t launch_delta_t(const short *o, const short *dout, float *delta, int64_t B, int64_t Sq, int64_t Hq,
-                                 hipStream_t st) {
+static hipError_t launch_delta_t(const short *o, const short *dout, float *delta, const float *lse_in, float *lse_out,
+                                 int64_t B, int64_t Sq, int64_t Hq, hipStream_t st) {
   constexpr int RPB = 256 / (DV / 8);
   const int64_t rows = B * Sq * Hq;
   int64_t blocks = (rows + RPB - 1) / RPB;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL((delta_kernel<TT, DV>), dim3((unsigned)blocks), dim3(256), 0, st, o, dout, delta, rows, (int)Sq,
-                     (int)Hq);
+  hipLaunchKernelGGL((delta_kernel<TT, DV>), dim3((unsigned)blocks), dim3(256), 0, st, o, dout, delta, lse_in, lse_out,
+                     rows, (int)Sq, (int)Hq);
   return hipGetLastError();
 }
 
-hipError_t launch_delta(const short *o, const short *dout, float *delta, int64_t B, int64_t Sq, int64_t Hq,
-                        int64_t Dv, bool bf16, hipStream_t st) {
-#define DISPATCH_DV(N)                                                                   \
-  case N:                                                                                \
-    return bf16 ? launch_delta_t<BF16, N>(o, dout, delta, B, Sq, Hq, st)                 \
-                : launch_delta_t<F16, N>(o, dout, delta, B, Sq, Hq, st);
+hipError_t launch_delta(const short *o, const short *dout, float *delta, const float *lse_in, float *lse_out,
+                        int64_t B, int64_t Sq, int64_t Hq, int64_t Dv, bool bf16, hipStream_t st) {
+#define DISPATCH_DV(N)                                                                       \
+  case N:                                                                                    \
+    return bf16 ? launch_delta_t<BF16, N>(o, dout, delta, lse_in, lse_out, B, Sq, Hq, st)    \
+                : launch_delta_t<F16, N>(o, dout, delta, lse_in, lse_out, B, Sq, Hq, st);
   switch (Dv) {
     DISPATCH_DV(64)
     DISPATCH_DV(128)

@@ -120,6 +120,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cold-iters", type=int, default=10)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a known-size kernel "
+                         "against which profiler byte counters are scaled)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this backward needs no inter-GPU communication; "
@@ -186,6 +189,13 @@ def main():
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1) * 1e3)
     del flush
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     npairs = pairs(w)
     flops = 2.5 * npairs * (2 * w.Dqk + 2 * w.Dv)

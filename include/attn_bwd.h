@@ -88,7 +88,7 @@ typedef struct {
 } attn_bwd_args;
 
 /* Bytes of workspace the call needs for these sizes (0 if the arguments are invalid).
- * Dense: delta [B,Hq,Sq] f32.  Top-k: delta plus dK/dV f32 accumulators at Hkv heads.
+ * Dense: delta and a sanitised copy of lse, [B,Hq,Sq] f32 each.
  * Never an Hq-shaped dK/dV buffer. */
 size_t attn_bwd_workspace_size(const attn_bwd_args *a);
 

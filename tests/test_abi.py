@@ -39,10 +39,10 @@ def valid_args(**kw):
 
 
 def test_workspace_size():
-    assert ab.attn_bwd_workspace_size(valid_args()) == 2 * 32 * 2048 * 4
+    assert ab.attn_bwd_workspace_size(valid_args()) == 2 * (2 * 32 * 2048 * 4)
     # never Hq-shaped dK/dV: GQA needs the same delta-only workspace
-    assert ab.attn_bwd_workspace_size(valid_args(Hkv=4)) == 2 * 32 * 2048 * 4
-    assert ab.attn_bwd_workspace_size(valid_args(B=1, Sq=3, Hq=2, Hkv=2)) == 256  # 256-byte granularity
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=4)) == 2 * (2 * 32 * 2048 * 4)
+    assert ab.attn_bwd_workspace_size(valid_args(B=1, Sq=3, Hq=2, Hkv=2)) == 512  # 256-byte granularity
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=5)) == 0
 
 
