@@ -73,11 +73,22 @@ __device__ __forceinline__ s4v lds_tr4(const short *p) {
 __device__ __forceinline__ s8v cat8(s4v a, s4v b) { return s8v{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 
 // LDS tiles are stored without row padding; the 16-byte chunk c of row R sits at chunk
-// c ^ swz(R).  swz takes 8 distinct values over any 8 aligned rows (so a ds_read_b128 of one
-// chunk across rows R..R+7 touches 8 distinct chunks = all banks once) and 4 distinct values
-// of swz/2 over any 4 aligned rows (so a transposed read of 32 bytes from each of rows
-// R..R+3 touches 4 distinct 32-byte slots).
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+// c ^ swz<D>(R).  gfx950's LDS serves 256 bytes (64 banks) per cycle, i.e. 16 lanes of a
+// ds_read_b128 or 32 lanes of a ds_read_tr16_b64 (measured: the transposed reads of these
+// kernels run at 62 / 119 / 192 B/clk/CU with no swizzle / a 32-bank swizzle / this one).
+//   D = 128 (256-byte rows, one per bank line): swz takes 16 distinct values over 16 aligned
+//     rows (the 16 lanes of a b128 read of one chunk hit 16 distinct chunk positions), and
+//     swz/4 takes 4 distinct values over 4 aligned rows (the 32 lanes of a transposed read
+//     cover 4 rows x 4 chunks, which land in 4 disjoint groups of 4 positions).
+//   D = 64 (128-byte rows, two per bank line): the row parity picks the half line and
+//     swz(R) = f(R/2) with f bijective on 8 values, and f(x), f(x+1) differing in bit 2 for
+//     even x, which gives the same two properties.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(D == 64 || D == 128, "swizzle defined for 64- and 128-wide rows");
+  if (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
+  return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
 
 // Asynchronous 16-byte copy global -> LDS: lane l of the wave writes lds_base + 16*l.
 // lds_base must be wave-uniform.  Completion is tracked by vmcnt (wait_vm0 below).

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
 #pragma unroll
     for (int u = 0; u < C::WIW; u++) {
       const int slot0 = (w * C::WIW + u) * 64;
-      const int s = slot0 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz(row);
+      const int s = slot0 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz<D>(row);
       const int qi = min(q0 + row, p.Sq - 1);
       const int64_t o64 = ((int64_t)(b * p.Sq + qi) * p.Hq + h) * D + 8 * ch;
       g2lds16(p.q + o64, &q_s[buf][slot0 * 8]);
@@ -115,15 +115,16 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
   };
 
   // Per-lane LDS offsets (elements): natural read of query row 32*mb + lo, logical chunk
-  // 2*kk + hi; transposed read of rows 16*ks + 4*hi + i16/4 (+8), columns 32*dn + 16*(g16&1) +
-  // 4*(i16&3).
-  const int sw_lo = swz(lo);
+  // 2*kk + hi; transposed read of rows 16*ks + 8*half + 4*hi + i16/4, columns 32*dn +
+  // 16*(g16&1) + 4*(i16&3).  The swizzle has period 16 in the row, so rows lo and 32*mb + lo
+  // share it while the two halves of a transposed read need their own.
+  const int sw_lo = swz<D>(lo);
   const int tr_row = 4 * hi + (i16 >> 2);
-  const int sw_tr = swz(tr_row);
+  const int sw_tr0 = swz<D>(tr_row), sw_tr1 = swz<D>(tr_row + 8);
   auto nat_off = [&](int mb, int kk) { return (32 * mb + lo) * D + 8 * ((2 * kk + hi) ^ sw_lo); };
-  auto tr_off = [&](int ks, int dn) {
-    const int ch = (4 * dn + 2 * (g16 & 1) + ((i16 & 3) >> 1)) ^ sw_tr;
-    return (16 * ks + tr_row) * D + 8 * ch + 4 * (i16 & 1);
+  auto tr_off = [&](int ks, int dn, int half) {
+    const int ch = (4 * dn + 2 * (g16 & 1) + ((i16 & 3) >> 1)) ^ (half ? sw_tr1 : sw_tr0);
+    return (16 * ks + 8 * half + tr_row) * D + 8 * ch + 4 * (i16 & 1);
   };
 
   if (nsteps > 0) issue(0, 0);
@@ -207,8 +208,7 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
       for (int ks = 0; ks < C::KS; ks++)
 #pragma unroll
         for (int dn = 0; dn < C::ND; dn++) {
-          const short *bp = &bsrc[tr_off(ks, dn)];
-          const s8v bb = cat8(lds_tr4(bp), lds_tr4(bp + 8 * D));
+          const s8v bb = cat8(lds_tr4(&bsrc[tr_off(ks, dn, 0)]), lds_tr4(&bsrc[tr_off(ks, dn, 1)]));
           acc[dn] = TT::mfma(pa[ks], bb, acc[dn]);
           if (TT::SPLIT) acc[dn] = TT::mfma(pl[ks], bb, acc[dn]);
         }

@@ -93,14 +93,14 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   const int wlast = min(qw0 + 32, p.Sq) - 1;  // last valid query row of this wave
 
   // Direct global->LDS tile loads: slot s of a tile is physical chunk s % CPR of row s / CPR and
-  // holds logical chunk (s % CPR) ^ swz(row).  Rows past the end are clamped to the last key
+  // holds logical chunk (s % CPR) ^ swz<D>(row).  Rows past the end are clamped to the last key
   // (their scores are masked).
   auto issue = [&](int t, int buf) {
     const int k0 = (kb_lo + t) * BK;
 #pragma unroll
     for (int u = 0; u < C::WIW; u++) {
       const int slot0 = (w * C::WIW + u) * 64;
-      const int s = slot0 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz(row);
+      const int s = slot0 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz<D>(row);
       const int kj = min(k0 + row, p.Skv - 1);
       const int64_t o64 = ((int64_t)(b * p.Skv + kj) * p.Hkv + g) * D + 8 * ch;
       g2lds16(p.k + o64, &k_s[buf][slot0 * 8]);
@@ -109,15 +109,16 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   };
 
   // Per-lane LDS offsets (elements): natural read of key row 32*kb + lo, logical chunk
-  // 2*kk + hi; transposed read of rows 16*kst + 4*hi + i16/4 (+8), columns 32*dn + 16*(g16&1)
-  // + 4*(i16&3).
-  const int sw_lo = swz(lo);
+  // 2*kk + hi; transposed read of rows 16*kst + 8*half + 4*hi + i16/4, columns 32*dn +
+  // 16*(g16&1) + 4*(i16&3).  The swizzle has period 16 in the row, so rows lo and 32*kb + lo
+  // share it while the two halves of a transposed read need their own.
+  const int sw_lo = swz<D>(lo);
   const int tr_row = 4 * hi + (i16 >> 2);
-  const int sw_tr = swz(tr_row);
+  const int sw_tr0 = swz<D>(tr_row), sw_tr1 = swz<D>(tr_row + 8);
   auto nat_off = [&](int kb, int kk) { return (32 * kb + lo) * D + 8 * ((2 * kk + hi) ^ sw_lo); };
-  auto tr_off = [&](int kst, int dn) {
-    const int ch = (4 * dn + 2 * (g16 & 1) + ((i16 & 3) >> 1)) ^ sw_tr;
-    return (16 * kst + tr_row) * D + 8 * ch + 4 * (i16 & 1);
+  auto tr_off = [&](int kst, int dn, int half) {
+    const int ch = (4 * dn + 2 * (g16 & 1) + ((i16 & 3) >> 1)) ^ (half ? sw_tr1 : sw_tr0);
+    return (16 * kst + 8 * half + tr_row) * D + 8 * ch + 4 * (i16 & 1);
   };
 
   if (nsteps > 0) issue(0, 0);
@@ -175,8 +176,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
       for (int kst = 0; kst < C::KST; kst++)
 #pragma unroll
         for (int dn = 0; dn < C::ND; dn++) {
-          const short *bp = &ks[tr_off(kst, dn)];
-          const s8v bb = cat8(lds_tr4(bp), lds_tr4(bp + 8 * D));
+          const s8v bb = cat8(lds_tr4(&ks[tr_off(kst, dn, 0)]), lds_tr4(&ks[tr_off(kst, dn, 1)]));
           acc[dn] = TT::mfma(da[kst], bb, acc[dn]);
           if (TT::SPLIT) acc[dn] = TT::mfma(dl[kst], bb, acc[dn]);
         }

@@ -121,8 +121,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cold-iters", type=int, default=10)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="after timing, run one plain device copy of this many MiB (a known-size kernel "
-                         "against which profiler byte counters are scaled)")
+                    help="after timing, run one fp16->f32 device copy reading this many MiB (a known-size "
+                         "kernel against which profiler byte counters are scaled)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this backward needs no inter-GPU communication; "
@@ -190,8 +190,10 @@ def main():
         cold.append(e0.elapsed_time(e1) * 1e3)
     del flush
     if args.calib_copy_mib:
-        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
+        # fp16 -> f32 conversion copy: reads 2 bytes and writes 4 bytes per element, so it runs a
+        # plain elementwise kernel (a same-dtype copy would be a DMA transfer, not a kernel).
+        src = torch.ones(args.calib_copy_mib << 19, dtype=torch.float16, device=dev)
+        dst = torch.empty(src.shape, dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
