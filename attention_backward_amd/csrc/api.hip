@@ -3,7 +3,8 @@
 // Validates every argument on the host before anything is enqueued, carves the workspace,
 // and enqueues the kernels on the caller's stream:
 //   dense:  delta (preprocess) -> dK/dV (KV-block owned) -> dQ (query-block owned)
-//   top-k:  not built yet (ATTN_E_UNSUPPORTED).
+//   top-k:  zero the f32 dK/dV accumulators, delta -> gathered backward (dQ owned, dK/dV
+//           added into the accumulators) -> landing (scale, cast).
 // The library keeps no state between calls.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -41,14 +42,25 @@ int validate_sizes(const attn_bwd_args *a) {
   // 32-bit row indices inside the kernels: every row count must fit comfortably.
   const int64_t lim = (int64_t)1 << 31;
   if (a->B * a->Sq * a->Hq >= lim || a->B * a->Skv * a->Hkv >= lim) return ATTN_E_UNSUPPORTED;
-  if (a->topk_idx) return ATTN_E_UNSUPPORTED;  // the gathered top-k kernels are not built yet
-  if (!((a->Dqk == 64 && a->Dv == 64) || (a->Dqk == 128 && a->Dv == 128))) return ATTN_E_UNSUPPORTED;
+  if (a->topk_idx) {
+    if (a->topk >= lim) return ATTN_E_UNSUPPORTED;
+    if (!(a->Dqk == 576 && a->Dv == 512)) return ATTN_E_UNSUPPORTED;
+  } else if (!((a->Dqk == 64 && a->Dv == 64) || (a->Dqk == 128 && a->Dv == 128))) {
+    return ATTN_E_UNSUPPORTED;
+  }
   return ATTN_OK;
 }
 
-// Workspace: delta [B,Hq,Sq] f32, then the sanitised lse [B,Hq,Sq] f32, each 256-byte aligned.
+// Workspace, each part 256-byte aligned: delta [B,Hq,Sq] f32, the sanitised lse [B,Hq,Sq] f32,
+// and for the top-k path the accumulators dK_acc [B,Skv,Hkv,Dqk] and dV_acc [B,Skv,Hkv,Dv] f32.
 size_t row_stat_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Hq * a->Sq) * sizeof(float)); }
-size_t workspace_bytes_for(const attn_bwd_args *a) { return 2 * row_stat_bytes(a); }
+size_t dk_acc_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Skv * a->Hkv * a->Dqk) * 4); }
+size_t dv_acc_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Skv * a->Hkv * a->Dv) * 4); }
+size_t workspace_bytes_for(const attn_bwd_args *a) {
+  size_t n = 2 * row_stat_bytes(a);
+  if (a->topk_idx) n += dk_acc_bytes(a) + dv_acc_bytes(a);
+  return n;
+}
 
 }  // namespace
 
@@ -65,6 +77,7 @@ int attn_bwd_ex(const attn_bwd_args *a) {
   const void *ptrs[] = {a->q, a->k, a->v, a->o, a->dout, a->lse, a->dq, a->dk, a->dv};
   for (const void *p : ptrs)
     if (!p || !aligned16(p)) return ATTN_E_INVAL;
+  if (a->topk_idx && ((uintptr_t)a->topk_idx & 3) != 0) return ATTN_E_INVAL;
   const size_t need = workspace_bytes_for(a);
   if (a->workspace) {
     if (((uintptr_t)a->workspace & 255) != 0) return ATTN_E_INVAL;
@@ -111,11 +124,24 @@ int attn_bwd_ex(const attn_bwd_args *a) {
   hipError_t e = ev ? hipEventRecord(ev[0], st) : hipSuccess;
   if (e == hipSuccess)
     e = attn::launch_delta(p.o, p.dout, p.delta, a->lse, (float *)p.lse, a->B, a->Sq, a->Hq, a->Dv, bf16, st);
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-  if (e == hipSuccess) e = attn::launch_dense_dkdv(p, bf16, st);
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
-  if (e == hipSuccess) e = attn::launch_dense_dq(p, bf16, st);
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
+  if (!a->topk_idx) {
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+    if (e == hipSuccess) e = attn::launch_dense_dkdv(p, bf16, st);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+    if (e == hipSuccess) e = attn::launch_dense_dq(p, bf16, st);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
+  } else {
+    float *dk_acc = (float *)((char *)ws + 2 * row_stat_bytes(a));
+    float *dv_acc = (float *)((char *)dk_acc + dk_acc_bytes(a));
+    const int64_t nk = a->B * a->Skv * a->Hkv * a->Dqk, nv = a->B * a->Skv * a->Hkv * a->Dv;
+    if (e == hipSuccess) e = attn::launch_zero(dk_acc, (int64_t)((dk_acc_bytes(a) + dv_acc_bytes(a)) / 4), st);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+    if (e == hipSuccess) e = attn::launch_sparse_bwd(p, dk_acc, dv_acc, bf16, st);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+    if (e == hipSuccess) e = attn::launch_land(dk_acc, p.dk, nk, a->scale, bf16, st);
+    if (e == hipSuccess) e = attn::launch_land(dv_acc, p.dv, nv, 1.0f, bf16, st);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
+  }
   if (!a->workspace) {
     hipError_t e2 = hipFreeAsync(ws, st);
     if (e == hipSuccess && e2 != hipSuccess) return set_hip_error(e2, "hipFreeAsync(workspace)");

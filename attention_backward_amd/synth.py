@@ -83,13 +83,15 @@ def round_to(x: np.ndarray, dtype: str) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DTYPES[dtype])
 
 
-def draw_topk(rng: np.random.Generator, B: int, Sq: int, Skv: int, Hkv: int, topk: int) -> np.ndarray:
-    """Distinct key indices per (b, i, g), uniform over [0, i + Skv - Sq], in draw order."""
+def draw_topk(rng: np.random.Generator, B: int, Sq: int, Skv: int, Hkv: int, topk: int,
+              causal: bool = True) -> np.ndarray:
+    """Distinct key indices per (b, i, g), uniform over the keys query i may see ([0, i + Skv - Sq]
+    when causal, else [0, Skv)), in draw order."""
     off = Skv - Sq
     idx = np.empty((B, Sq, Hkv, topk), np.int32)
     for b in range(B):
         for i in range(Sq):
-            n = i + off + 1
+            n = max(0, min(Skv, i + off + 1)) if causal else Skv
             for g in range(Hkv):
                 if n >= topk:
                     idx[b, i, g] = rng.choice(n, size=topk, replace=False)
@@ -114,5 +116,5 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
         "idx": None,
     }
     if w.topk:
-        out["idx"] = torch.from_numpy(draw_topk(rng, w.B, w.Sq, w.Skv, w.Hkv, w.topk))
+        out["idx"] = torch.from_numpy(draw_topk(rng, w.B, w.Sq, w.Skv, w.Hkv, w.topk, w.causal))
     return out

@@ -44,6 +44,9 @@ def test_workspace_size():
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=4)) == 2 * (2 * 32 * 2048 * 4)
     assert ab.attn_bwd_workspace_size(valid_args(B=1, Sq=3, Hq=2, Hkv=2)) == 512  # 256-byte granularity
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=5)) == 0
+    # top-k: delta and lse rows, then f32 dK/dV accumulators at Hkv
+    a = valid_args(topk_idx=0x100000, topk=2048, B=1, Sq=4096, Skv=8192, Hq=64, Hkv=1, Dqk=576, Dv=512)
+    assert ab.attn_bwd_workspace_size(a) == 2 * (64 * 4096 * 4) + 8192 * 576 * 4 + 8192 * 512 * 4
 
 
 @pytest.mark.parametrize(
@@ -64,7 +67,11 @@ def test_workspace_size():
         (dict(topk=4), -1),               # topk without an index list
         (dict(Dqk=96, Dv=96), -2),        # no kernel for this head dim
         (dict(Dqk=128, Dv=64), -2),
-        (dict(topk_idx=0x100000, topk=8), -2),  # top-k kernels not built yet
+        (dict(topk_idx=0x100000, topk=8), -2),  # top-k kernels exist for Dqk=576, Dv=512 only
+        (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, window=4), -1),  # no window with top-k
+        (dict(topk_idx=0x100002, topk=8, Dqk=576, Dv=512), -1),  # misaligned index list
+        (dict(topk_idx=0x100000, topk=0, Dqk=576, Dv=512), -1),
+        (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, workspace=0x100000, workspace_bytes=1 << 20), -3),
         (dict(workspace=0x100000, workspace_bytes=16), -3),
         (dict(workspace=0x100080, workspace_bytes=1 << 30), -1),  # workspace not 256-byte aligned
         (dict(workspace=0, workspace_bytes=64), -1),

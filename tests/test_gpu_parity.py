@@ -37,10 +37,11 @@ def run(inp, w):
 
 def full_compare(w, inp=None):
     log(f"case {w.name}: B={w.B} Sq={w.Sq} Skv={w.Skv} Hq={w.Hq} Hkv={w.Hkv} D={w.Dqk}/{w.Dv} {w.dtype} "
-        f"causal={w.causal} window={w.window}")
+        f"causal={w.causal} window={w.window} topk={w.topk}")
     inp = inp or prepare(w)
     dq, dk, dv = run(inp, w)
-    ref = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["o"], inp["dout"], inp["lse"], w.scale, w.causal, w.window)
+    ref = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["o"], inp["dout"], inp["lse"], w.scale, w.causal, w.window,
+                     inp["idx"])
     for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         check_close(name, got.double().numpy(), r)
     return inp, (dq, dk, dv)
@@ -146,16 +147,3 @@ def test_full_size_sampled_parity(name):
     check_close("dv rows", got_dv, ref_dv)
     for t in (dq, dk, dv):
         assert torch.isfinite(t.float()).all()
-
-
-def test_topk_variant_reports_unsupported_until_built():
-    w = W["sparse_mla_b1_sq4096_skv8192_h64_dqk576_dv512_top2048_bf16"].with_(Sq=64, Skv=128, topk=16, Hq=64)
-    inp = synth.make_inputs(w)
-    g = {k: v.cuda() for k, v in inp.items() if v is not None}
-    o = torch.zeros_like(g["dout"])
-    lse = torch.zeros((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda")
-    dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
-    args = ab.make_args(g["q"], g["k"], g["v"], o, g["dout"], lse, dq, dk, dv, scale=w.scale, topk_idx=g["idx"])
-    with pytest.raises(ab.AttnBwdError) as e:
-        ab.attn_bwd_ex(args)
-    assert e.value.status == -2

@@ -1,0 +1,108 @@
+"""Parity of the top-k (gathered-KV) backward with the f64 oracle, through the C ABI.
+
+The index list of each (b, query i, kv head) is a multiset of keys: every occurrence counts once,
+entries < 0, >= Skv or (causal) past the diagonal are ignored, and fewer visible keys than topk
+leaves -1 padding (TileLang PR #2592 page, the sparse MLA backward; the oracle's reading).  dK and
+dV are summed with f32 atomics, so their bits may differ run to run; every run is held to the
+same tolerance, |gpu - ref| <= 5e-3 + 1e-2 |ref| elementwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_backward_amd import synth
+from tests.helpers import check_close, log, prepare, sample_rows
+from tests.test_gpu_parity import full_compare, run
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+C5 = "sparse_mla_b1_sq4096_skv8192_h64_dqk576_dv512_top2048_bf16"
+
+
+def sparse(name, **kw):
+    base = dict(B=1, Sq=70, Skv=150, Hq=64, Hkv=1, Dqk=576, Dv=512, dtype="bf16", causal=True, window=0, topk=100,
+                seed=200)
+    base.update(kw)
+    return synth.Workload(name=name, **base)
+
+
+SMALL = [
+    # topk not a multiple of the 32-slot chunk; queries i < 19 see fewer than 100 keys (-1 padding)
+    sparse("mla_h64_bf16_padded"),
+    # G = 8 < 32 query heads per workgroup block, two KV heads, B = 2, fp16
+    sparse("gqa_g8_fp16", B=2, Sq=40, Skv=64, Hq=16, Hkv=2, dtype="fp16", topk=48, seed=201),
+    # G = 40: a full block of 32 heads plus a block of 8; non-causal lists over every key
+    sparse("g40_noncausal", Sq=33, Skv=90, Hq=40, Hkv=1, causal=False, topk=64, seed=202),
+    # Sq > Skv: the first queries see no key at all (empty rows)
+    sparse("causal_sq_gt_skv", Sq=80, Skv=50, Hq=32, Hkv=1, topk=20, seed=203),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_sparse_small_full_parity(w):
+    inp = prepare(w)
+    _, (dq, dk, dv) = full_compare(w, inp)
+    # keys that no list selects get exactly zero gradients
+    idx = inp["idx"].numpy()
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            sel = np.zeros(w.Skv, bool)
+            for i in range(w.Sq):
+                for j in idx[b, i, g]:
+                    if 0 <= j < w.Skv and (not w.causal or j <= i + w.Skv - w.Sq):
+                        sel[j] = True
+            assert torch.all(dk[b, ~torch.from_numpy(sel), g] == 0)
+            assert torch.all(dv[b, ~torch.from_numpy(sel), g] == 0)
+
+
+def test_sparse_duplicates_and_out_of_range_entries():
+    """Each occurrence of a key counts; negative, too-large and (causal) future entries are dropped."""
+    w = sparse("dups", Sq=48, Skv=96, Hq=32, Hkv=1, topk=72, seed=210)
+    inp = synth.make_inputs(w)
+    rng = np.random.default_rng(211)
+    idx = inp["idx"].numpy().copy()
+    Sq, Skv, off = w.Sq, w.Skv, w.Skv - w.Sq
+    for i in range(Sq):
+        row = idx[0, i, 0]
+        vis = i + off + 1
+        row[:10] = rng.integers(0, vis, 10)           # repeats of visible keys
+        row[10:14] = row[0]                            # one key four more times
+        row[14] = -7                                   # negative
+        row[15] = Skv + 3                              # past the end
+        row[16] = min(Skv - 1, i + off + 1 + int(rng.integers(0, 5)))  # future key (ignored when causal)
+        if i + off + 1 >= Skv:
+            row[16] = -1
+    inp["idx"] = torch.from_numpy(idx)
+    from oracle import forward as oracle_forward
+
+    inp["o"], inp["lse"] = oracle_forward.make_o_lse(w, inp)
+    full_compare(w, inp)
+
+
+def test_sparse_full_size_sampled_parity():
+    """The full top-k workload in the benchmark's launch configuration, on sampled rows."""
+    w = W[C5]
+    log(f"case {C5} (full size, sampled rows)")
+    inp = prepare(w)
+    dq, dk, dv = run(inp, w)
+    rng = np.random.default_rng(9)
+    qrows = sample_rows(rng, 32, w.B, w.Sq, w.Hq)
+    # key rows: edges, the last keys (selected by few queries) and random ones
+    krows = sample_rows(rng, 32, w.B, w.Skv, w.Hkv, extra_i=(w.Skv - 3, w.Skv // 2))
+    args = (inp["q"], inp["k"], inp["v"], inp["o"], inp["dout"], inp["lse"], w.scale)
+    ref_dq = oracle.bwd_dq_rows(*args, qrows, w.causal, w.window, inp["idx"])
+    ref_dk, ref_dv = oracle.bwd_dkv_rows(*args, krows, w.causal, w.window, inp["idx"])
+    check_close("dq rows", dq[qrows[:, 0], qrows[:, 1], qrows[:, 2]].double().numpy(), ref_dq)
+    check_close("dk rows", dk[krows[:, 0], krows[:, 1], krows[:, 2]].double().numpy(), ref_dk)
+    check_close("dv rows", dv[krows[:, 0], krows[:, 1], krows[:, 2]].double().numpy(), ref_dv)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    # unattended keys: exactly zero
+    idx = inp["idx"].numpy().reshape(-1)
+    sel = np.zeros(w.Skv, bool)
+    sel[idx[idx >= 0]] = True
+    log(f"  {int((~sel).sum())} keys selected by no query")
+    unsel = torch.from_numpy(~sel)
+    assert torch.all(dk[0, unsel] == 0) and torch.all(dv[0, unsel] == 0)
