@@ -34,6 +34,36 @@ LOG2E = 1.4426950408889634
 METRIC = "attn-bwd TFLOP/s (causal-adjusted) + % of MI355X fp16/bf16 MFMA peak"
 
 
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 counter runs (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch), each scaled by what the counter reads for an fp16->f32 copy of
+# known size (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000).  Keyed by the hash of the kernel's source
+# files at the time: once the sources change, the figure no longer applies and is reported as null.
+PROFILED_TRAFFIC = {
+    ("dense_dkdv", "mha_causal_b2_s2048_h32_d128_fp16"): dict(
+        fetch_kib=111119.2, write_kib=65536.0, fetch_scale=2.000, write_scale=1.000,
+        files=("dense_dkdv.hip", "common.h"), sha="2ea69d80ca6aa921"),
+    ("sparse_bwd", "sparse_mla_b1_sq4096_skv8192_h64_dqk576_dv512_top2048_bf16"): dict(
+        fetch_kib=12862184.2, write_kib=71598080.3, fetch_scale=2.000, write_scale=1.000,
+        files=("sparse_bwd.hip", "common.h"), sha="12c0a67bbd876137"),
+}
+
+
+def profiled_traffic(kernel, workload):
+    """Calibrated HBM bytes per launch if counters were taken on the current kernel source, else None."""
+    import hashlib
+
+    rec = PROFILED_TRAFFIC.get((kernel, workload))
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for f in rec["files"]:
+        with open(os.path.join(ROOT, "attention_backward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != rec["sha"]:
+        return None
+    return round((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024)
+
+
 def pairs(w) -> int:
     off = w.Skv - w.Sq
     if w.topk:
@@ -44,7 +74,22 @@ def pairs(w) -> int:
     return int(np.maximum(0, hi - lo + 1).sum()) * w.B * w.Hq
 
 
-def gpu_forward_inputs(q, k, v, w):
+def _softmax_out(s, ok, vv):
+    """Masked base-2 softmax of score rows s (-> O rows and lse), fp32 on the GPU."""
+    s = torch.where(ok, s, torch.full_like(s, -math.inf))
+    m = s.amax(-1, keepdim=True)
+    empty = torch.isinf(m) & (m < 0)
+    m = torch.where(empty, torch.zeros_like(m), m)
+    p = torch.exp2(s - m)
+    tot = p.sum(-1, keepdim=True)
+    safe = torch.where(empty, torch.ones_like(tot), tot)
+    out = (p @ vv) if vv.dim() == 2 else torch.bmm(p, vv)
+    o = torch.where(empty, torch.zeros_like(out), out / safe)
+    lse = torch.where(empty, torch.full_like(m, -math.inf), m + torch.log2(safe)).squeeze(-1)
+    return o, lse
+
+
+def gpu_forward_inputs(q, k, v, w, idx=None):
     """Input preparation (not timed): O in the storage dtype and base-2 lse in f32 of the masked
     softmax forward over the drawn inputs, evaluated with torch fp32 matmuls on the GPU."""
     B, Sq, Hq, _ = q.shape
@@ -54,6 +99,27 @@ def gpu_forward_inputs(q, k, v, w):
     c = w.scale * LOG2E
     o = torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if idx is not None:  # top-k: each query row against its own gathered keys, all G heads at once
+        rows = 64
+        for b in range(B):
+            for g in range(Hkv):
+                kk = k[b, :, g].float()
+                vv = v[b, :, g].float()
+                for i0 in range(0, Sq, rows):
+                    i1 = min(Sq, i0 + rows)
+                    ix = idx[b, i0:i1, g].long()
+                    ok = (ix >= 0) & (ix < Skv)
+                    if w.causal:
+                        ok &= ix <= torch.arange(i0, i1, device=q.device).unsqueeze(1) + off
+                    ixc = torch.where(ok, ix, torch.zeros_like(ix))
+                    kt = kk[ixc].transpose(1, 2).contiguous()              # [n, Dqk, topk]
+                    vs = vv[ixc].contiguous()                              # [n, topk, Dv]
+                    qq = q[b, i0:i1, g * G:(g + 1) * G].float().contiguous()  # [n, G, Dqk]
+                    s_ = torch.bmm(qq, kt) * c                             # [n, G, topk]
+                    oo, ll = _softmax_out(s_, ok.unsqueeze(1).expand_as(s_), vs)
+                    o[b, i0:i1, g * G:(g + 1) * G] = oo.to(q.dtype)
+                    lse[b, g * G:(g + 1) * G, i0:i1] = ll.t()
+        return o, lse
     rows = 1024
     for b in range(B):
         for h in range(Hq):
@@ -63,23 +129,17 @@ def gpu_forward_inputs(q, k, v, w):
             qq = q[b, :, h].float()
             for i0 in range(0, Sq, rows):
                 i1 = min(Sq, i0 + rows)
-                s = (qq[i0:i1] @ kt) * c
+                s_ = (qq[i0:i1] @ kt) * c
                 ii = torch.arange(i0, i1, device=q.device).unsqueeze(1)
                 jj = torch.arange(Skv, device=q.device).unsqueeze(0)
-                ok = torch.ones_like(s, dtype=torch.bool)
+                ok = torch.ones_like(s_, dtype=torch.bool)
                 if w.causal:
                     ok &= jj <= ii + off
                 if w.window > 0:
                     ok &= jj > ii + off - w.window
-                s = torch.where(ok, s, torch.full_like(s, -math.inf))
-                m = s.amax(1, keepdim=True)
-                empty = torch.isinf(m) & (m < 0)
-                m = torch.where(empty, torch.zeros_like(m), m)
-                p = torch.exp2(s - m)
-                tot = p.sum(1, keepdim=True)
-                safe = torch.where(empty, torch.ones_like(tot), tot)
-                o[b, i0:i1, h] = torch.where(empty, torch.zeros_like(tot), (p @ vv) / safe).to(q.dtype)
-                lse[b, h, i0:i1] = torch.where(empty, torch.full_like(m, -math.inf), m + torch.log2(safe)).squeeze(1)
+                oo, ll = _softmax_out(s_, ok, vv)
+                o[b, i0:i1, h] = oo.to(q.dtype)
+                lse[b, h, i0:i1] = ll
     return o, lse
 
 
@@ -101,6 +161,8 @@ def cpu_baseline(w, inp_cpu, target_s):
         oracle.bwd(*args, w.scale, w.causal, w.window)
         return time.perf_counter() - t0, nh
 
+    if w.topk:
+        return cpu_baseline_topk(w, inp_cpu, target_s, threads)
     dt1, nh1 = run(w.G)
     nh = min(w.Hq, max(nh1, int(nh1 * target_s / max(dt1, 1e-3))))
     dt, nh = run(nh) if nh > nh1 else (dt1, nh1)
@@ -109,6 +171,31 @@ def cpu_baseline(w, inp_cpu, target_s):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"full f64 backward of batch 0, query heads 0..{nh - 1} of {w.Hq} ({nh}/{w.B * w.Hq} of the "
                       f"workload's heads), {dt:.1f} s", "seconds": dt}
+
+
+def cpu_baseline_topk(w, inp_cpu, target_s, threads):
+    """Top-k workload: the oracle's full backward over the last n query rows of batch 0 with all
+    heads and every key (the last rows keep their causal diagonal, i + Skv - Sq, unchanged)."""
+    import oracle
+
+    def run(n):
+        i0 = w.Sq - n
+        args = (inp_cpu["q"][:1, i0:].contiguous(), inp_cpu["k"][:1].contiguous(), inp_cpu["v"][:1].contiguous(),
+                inp_cpu["o"][:1, i0:].contiguous(), inp_cpu["dout"][:1, i0:].contiguous(),
+                inp_cpu["lse"][:1, :, i0:].contiguous())
+        t0 = time.perf_counter()
+        oracle.bwd(*args, w.scale, w.causal, w.window, inp_cpu["idx"][:1, i0:].contiguous())
+        return time.perf_counter() - t0
+
+    n1 = 4
+    dt1 = run(n1)
+    n = min(w.Sq, max(n1, int(n1 * target_s / max(dt1, 1e-3))))
+    dt = run(n) if n > n1 else dt1
+    flops = 2.5 * n * w.Hq * w.topk * (2 * w.Dqk + 2 * w.Dv)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"full f64 backward of batch 0, the last {n} of {w.Sq} query rows with all {w.Hq} heads and "
+                      f"their top-{w.topk} lists ({n}/{w.B * w.Sq} of the workload's rows), {dt:.1f} s",
+            "seconds": dt}
 
 
 def main():
@@ -132,15 +219,14 @@ def main():
     import attention_backward_amd as ab
 
     w = synth.WORKLOADS[args.workload]
-    if w.topk:
-        print(f"{w.name}: the top-k kernels are not built yet", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
     inp = synth.make_inputs(w)
     q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
-    o, lse = gpu_forward_inputs(q, k, v, w)
+    idx = inp["idx"].to(dev) if w.topk else None
+    o, lse = gpu_forward_inputs(q, k, v, w, idx)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    a = ab.make_args(q, k, v, o, do, lse, dq, dk, dv, scale=w.scale, causal=w.causal, window=w.window)
+    a = ab.make_args(q, k, v, o, do, lse, dq, dk, dv, scale=w.scale, causal=w.causal, window=w.window,
+                     topk_idx=idx)
     need = ab.attn_bwd_workspace_size(a)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), need
@@ -168,11 +254,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     a.events = None
-    per = {"delta": [], "dkdv": [], "dq": [], "call": []}
+    # The library records its events between its phases: dense = preprocess | dK/dV kernel |
+    # dQ kernel; top-k = preprocess + accumulator zero-fill | gathered kernel | landing pass.
+    names = ("delta", "dkdv", "dq") if not w.topk else ("preprocess", "sparse_main", "landing")
+    per = {n_: [] for n_ in names + ("call",)}
     for row in ev:
-        per["delta"].append(row[0].elapsed_time(row[1]) * 1e3)
-        per["dkdv"].append(row[1].elapsed_time(row[2]) * 1e3)
-        per["dq"].append(row[2].elapsed_time(row[3]) * 1e3)
+        for j, n_ in enumerate(names):
+            per[n_].append(row[j].elapsed_time(row[j + 1]) * 1e3)
         per["call"].append(row[0].elapsed_time(row[3]) * 1e3)
     ms_per_step = wall * 1e3 / args.steps
 
@@ -205,10 +293,34 @@ def main():
     esz = 2
     med = {kname: statistics.median(vals) for kname, vals in per.items()}
     mean = {kname: statistics.fmean(vals) for kname, vals in per.items()}
-    dkdv_flops = npairs * (4 * w.Dqk + 4 * w.Dv)   # S, dP, dV, dK products
-    dq_flops = npairs * (4 * w.Dqk + 2 * w.Dv)     # S, dP recomputed, dQ
     delta_bytes = 2 * w.B * w.Sq * w.Hq * w.Dv * esz + 4 * w.B * w.Hq * w.Sq
-    dkdv_tf = dkdv_flops / (mean["dkdv"] * 1e-6) / 1e12
+    if not w.topk:
+        main_name = "dense_dkdv"
+        main_flops = npairs * (4 * w.Dqk + 4 * w.Dv)   # S, dP, dV, dK products
+        dq_flops = npairs * (4 * w.Dqk + 2 * w.Dv)     # S, dP recomputed, dQ
+        main_tf = main_flops / (mean["dkdv"] * 1e-6) / 1e12
+        kernels = {
+            "delta": {"us": round(mean["delta"], 2), "GB/s": round(delta_bytes / (mean["delta"] * 1e-6) / 1e9, 1),
+                      "frac_hbm": round(delta_bytes / (mean["delta"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+            "dkdv": {"us": round(mean["dkdv"], 2), "TFLOP/s": round(main_tf, 1)},
+            "dq": {"us": round(mean["dq"], 2), "TFLOP/s": round(dq_flops / (mean["dq"] * 1e-6) / 1e12, 1)},
+        }
+    else:
+        main_name = "sparse_bwd"
+        main_flops = npairs * (6 * w.Dqk + 4 * w.Dv)   # S, dP, dQ, dK, dV products over the listed pairs
+        main_tf = main_flops / (mean["sparse_main"] * 1e-6) / 1e12
+        acc_bytes = w.B * w.Skv * w.Hkv * (w.Dqk + w.Dv) * 4
+        pre_bytes = delta_bytes + acc_bytes                       # + the zero-fill of the accumulators
+        land_bytes = acc_bytes + w.B * w.Skv * w.Hkv * (w.Dqk + w.Dv) * esz
+        kernels = {
+            "preprocess": {"us": round(mean["preprocess"], 2),
+                           "GB/s": round(pre_bytes / (mean["preprocess"] * 1e-6) / 1e9, 1)},
+            "sparse_main": {"us": round(mean["sparse_main"], 2), "TFLOP/s": round(main_tf, 1),
+                            "atomic_payload_GB/s": round(npairs // w.G * (w.Dqk + w.Dv) * 4 * math.ceil(w.G / 32)
+                                                         / (mean["sparse_main"] * 1e-6) / 1e9, 1)},
+            "landing": {"us": round(mean["landing"], 2),
+                        "GB/s": round(land_bytes / (mean["landing"] * 1e-6) / 1e9, 1)},
+        }
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -222,27 +334,24 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic: N(0,1) q,k,v,dO from a seeded PCG64 generator; O and lse from an fp32 forward",
+        "data": "synthetic: N(0,1) q,k,v,dO from a seeded PCG64 generator" +
+                ("; top-k lists of distinct causal keys drawn uniformly" if w.topk else "") +
+                "; O and lse from an fp32 forward",
         "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal, "window": w.window, "topk": w.topk,
                    "metric_flops": flops, "pairs": npairs},
-        "roofline": {"kernel": "dense_dkdv", "bound": "mfma", "achieved": round(dkdv_tf, 2),
-                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(dkdv_tf / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flops_per_launch": dkdv_flops},
+        "roofline": {"kernel": main_name, "bound": "mfma", "achieved": round(main_tf, 2),
+                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(main_tf / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": profiled_traffic(main_name, w.name), "traffic_unit": "bytes per launch",
+                     "algorithmic_flops_per_launch": main_flops},
         "kernels_us_median": {kname: round(v_, 2) for kname, v_ in med.items()},
-        "kernels": {
-            "delta": {"us": round(mean["delta"], 2), "GB/s": round(delta_bytes / (mean["delta"] * 1e-6) / 1e9, 1),
-                      "frac_hbm": round(delta_bytes / (mean["delta"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
-            "dkdv": {"us": round(mean["dkdv"], 2), "TFLOP/s": round(dkdv_tf, 1)},
-            "dq": {"us": round(mean["dq"], 2),
-                   "TFLOP/s": round(dq_flops / (mean["dq"] * 1e-6) / 1e12, 1)},
-        },
+        "kernels": kernels,
         "cold_call_us": {"median": round(statistics.median(cold), 2), "min": round(min(cold), 2),
                          "max": round(max(cold), 2), "n": len(cold),
                          "tflops_at_median": round(flops / (statistics.median(cold) * 1e-6) / 1e12, 1)},
     }
     if not args.no_cpu_baseline:
-        inp_cpu = {n: inp[n] for n in ("q", "k", "v", "dout")}
+        inp_cpu = {n: inp[n] for n in ("q", "k", "v", "dout", "idx")}
         inp_cpu["o"], inp_cpu["lse"] = o.cpu(), lse.cpu()
         result["cpu_baseline"] = cpu_baseline(w, inp_cpu, args.cpu_seconds)
     print(json.dumps(result), flush=True)

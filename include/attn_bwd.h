@@ -82,14 +82,20 @@ typedef struct {
   size_t workspace_bytes;
   void *stream;                     /* hipStream_t                                             */
   void *events;                     /* optional, NULL or an array of 4 hipEvent_t created by the
-                                       caller: recorded on `stream` before the preprocess,
-                                       after it, after the dK/dV kernel and after the dQ kernel
-                                       (per-kernel timing without changing the work)          */
+                                       caller, recorded on `stream` between the phases: dense =
+                                       before the preprocess | after it | after the dK/dV kernel
+                                       | after the dQ kernel; top-k = before the preprocess |
+                                       after it and the accumulator zero-fill | after the
+                                       gathered kernel | after the landing passes (per-phase
+                                       timing without changing the work)                     */
 } attn_bwd_args;
 
-/* Bytes of workspace the call needs for these sizes (0 if the arguments are invalid).
- * Dense: delta and a sanitised copy of lse, [B,Hq,Sq] f32 each.
- * Never an Hq-shaped dK/dV buffer. */
+/* Bytes of workspace the call needs for these sizes (0 if the arguments are invalid), as
+ * 256-byte aligned parts:
+ *   delta and a sanitised copy of lse, [B,Hq,Sq] f32 each;
+ *   top-k only: f32 accumulators dK_acc [B,Skv,Hkv,Dqk] and dV_acc [B,Skv,Hkv,Dv].
+ * Never an Hq-shaped dK/dV buffer.  Top-k results: dq is written once per element; dk and dv
+ * are sums of f32 atomic additions, so their last bits may differ between identical calls. */
 size_t attn_bwd_workspace_size(const attn_bwd_args *a);
 
 /* The backward for the full argument set.  Returns an attn_status. */
@@ -97,7 +103,9 @@ int attn_bwd_ex(const attn_bwd_args *a);
 
 /* The same operation with Sq = Skv = S and Dqk = Dv = D, arguments in the order
  *   q, k, v, o, dout, lse, dq, dk, dv, B, S, Hq, Hkv, D, scale, causal, window, topk_idx,
- * followed by what the plain list cannot carry: topk, dtype, workspace, workspace_bytes, stream. */
+ * followed by what the plain list cannot carry: topk, dtype, workspace, workspace_bytes, stream.
+ * A single S and D cannot describe the top-k kernel's shapes (Sq != Skv, Dqk = 576 != Dv = 512):
+ * with topk_idx set it returns ATTN_E_UNSUPPORTED; use attn_bwd_ex for that path. */
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
              void *dq, void *dk, void *dv, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, float scale,
              int32_t causal, int32_t window, const int32_t *topk_idx, int64_t topk, int32_t dtype, void *workspace,
