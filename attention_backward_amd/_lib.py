@@ -48,12 +48,14 @@ _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """Load the library (raises if it has not been built)."""
+    """Load the library (raises if it has not been built).  ATTN_BWD_LIB may name another build
+    of the same library (e.g. one compiled with different tile parameters) to load instead."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_backward_amd.build`")
-        lib = ctypes.CDLL(LIB_PATH)
+        path = os.environ.get("ATTN_BWD_LIB") or LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m attention_backward_amd.build`")
+        lib = ctypes.CDLL(path)
         P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         lib.attn_bwd_workspace_size.argtypes = [ctypes.POINTER(attn_bwd_args)]
         lib.attn_bwd_workspace_size.restype = ctypes.c_size_t

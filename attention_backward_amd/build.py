@@ -1,9 +1,10 @@
 """Build libattn_bwd.so (HIP, gfx950) in-tree.
 
-    python -m attention_backward_amd.build
+    python -m attention_backward_amd.build [--out PATH] [-D NAME=VALUE ...]
 
 Compiles every csrc/*.hip for gfx950 with hipcc and links them into
-attention_backward_amd/libattn_bwd.so.  Packed-fp32 instruction selection is disabled
+attention_backward_amd/libattn_bwd.so (or PATH, with its objects beside it; -D passes a
+preprocessor definition, e.g. a tile parameter, to every file).  Packed-fp32 instruction selection is disabled
 (``-target-feature -packed-fp32-ops``); float atomics, where used, are the hardware ones.
 """
 from __future__ import annotations
@@ -38,31 +39,38 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *CFLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    build_dir = BUILD if out == LIB else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s_: _compile(s_, build_dir, defines), srcs))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import argparse
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=LIB)
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    a = ap.parse_args()
+    build(verbose=True, out=os.path.abspath(a.out), defines=a.defines)
     sys.exit(0)

@@ -102,6 +102,23 @@ __device__ __forceinline__ void g2lds4(const void *g, void *lds_base) {
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Keeps the compiler's scheduler from moving instructions across this point: an operand read
+// issued ahead of the products that consume it stays ahead of them (the scheduler otherwise
+// sinks such reads next to their use to save registers, which exposes the LDS latency).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Wave priority around MFMA sections (a scheduling hint between the waves sharing a SIMD: the
+// wave feeding the matrix core issues first, its partner's vector work fills the gaps).
+#ifndef ATTN_MFMA_PRIO
+#define ATTN_MFMA_PRIO 0
+#endif
+__device__ __forceinline__ void mfma_prio_hi() {
+  if (ATTN_MFMA_PRIO) __builtin_amdgcn_s_setprio(1);
+}
+__device__ __forceinline__ void mfma_prio_lo() {
+  if (ATTN_MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
+}
+
 // lse as the kernels use it: a row with lse = -inf (no allowed key) must give p = 0, so it is
 // mapped to +inf; exp2(x - inf) = 0.
 __device__ __forceinline__ float lse_fix(float l) { return l == -__builtin_inff() ? __builtin_inff() : l; }

@@ -29,6 +29,10 @@
 
 namespace attn {
 
+#ifndef ATTN_LDS_PREFETCH
+#define ATTN_LDS_PREFETCH 3
+#endif
+
 template <int D, int BN>
 struct DkdvCfg {
   static constexpr int NW = 8;                 // waves per workgroup
@@ -46,7 +50,7 @@ struct DkdvCfg {
 template <class TT, int D, int BN>
 __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
   using C = DkdvCfg<D, BN>;
-  __shared__ __attribute__((aligned(16))) short q_s[2][BN * D];
+  __shared__ __attribute__((aligned(16))) short q_s[3][BN * D];  // Q of steps t-1, t, t+1
   __shared__ __attribute__((aligned(16))) short do_s[2][BN * D];
   __shared__ __attribute__((aligned(16))) float lse_s[2][64];
   __shared__ __attribute__((aligned(16))) float dl_s[2][64];
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
 
   // Direct global->LDS loads of step t's Q/dO tile (rows past Sq are clamped to the last row;
   // the mask zeroes them) and of its lse/delta rows.
-  auto issue = [&](int t, int buf) {
+  auto issue = [&](int t, int qbuf, int buf) {
     const int q0 = (qb_lo + t / p.G) * BN;
     const int h = g * p.G + t % p.G;
 #pragma unroll
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
       const int s = slot0 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz<D>(row);
       const int qi = min(q0 + row, p.Sq - 1);
       const int64_t o64 = ((int64_t)(b * p.Sq + qi) * p.Hq + h) * D + 8 * ch;
-      g2lds16(p.q + o64, &q_s[buf][slot0 * 8]);
+      g2lds16(p.q + o64, &q_s[qbuf][slot0 * 8]);
       g2lds16(p.dout + o64, &do_s[buf][slot0 * 8]);
     }
     if (w < 2) {
@@ -127,41 +131,82 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
     return (16 * ks + 8 * half + tr_row) * D + 8 * ch + 4 * (i16 & 1);
   };
 
-  if (nsteps > 0) issue(0, 0);
+  // The two roles run separate copies of the step loop (same trip count, same barriers), so that
+  // registers live in one role's loop are not reserved in the other's.
+  //   P role:  S = Q K^T; P = exp2(S c - lse) masked -> LDS (f32) and A operands; | barrier |
+  //            dV += P^T dO; | barrier |
+  //   dS role: dK += dS^T Q of the previous step; dP = dO V^T; | barrier | dS = P (dP - delta)
+  //            from the partner's P; | barrier |
+  // The dS role applies dK one step late (dS kept in registers, Q of step t-1 in the third Q
+  // buffer), so it keeps the matrix core busy while its P-role partner on the same SIMD works
+  // through the softmax.
+  //
+  // A operands of phase 2, P^T or dS^T, A[m=key][k=query], with their low halves when
+  // TT::SPLIT: register 8*(ks%2)+e of block ks/2 is query 16*ks + 8*(e/4) + 4*hi + e%4, which
+  // matches the rows the transposed read of the B operand supplies.
+  auto pack = [&](s8v *pa, s8v *pl, int mb, int r, float x) {
+    const short xh = TT::cvt(x);
+    pa[2 * mb + (r >> 3)][r & 7] = xh;
+    pl[2 * mb + (r >> 3)][r & 7] = TT::SPLIT ? TT::cvt(x - TT::tof(xh)) : (short)0;
+  };
+  // acc += A^T B with B[k=query][n=d] read transposed from the row-major tile `src`.  The LDS
+  // operands are read PF products ahead through a ring of registers, so that the read latency
+  // hides behind the matrix core instead of stalling it before every product.
+  auto phase2 = [&](const s8v *pa, const s8v *pl, const short *src) {
+    constexpr int N = C::KS * C::ND, PF = ATTN_LDS_PREFETCH;
+    auto ld = [&](int n) {
+      const int ks = n / C::ND, dn = n % C::ND;
+      return cat8(lds_tr4(&src[tr_off(ks, dn, 0)]), lds_tr4(&src[tr_off(ks, dn, 1)]));
+    };
+    s8v ring[PF + 1];
+#pragma unroll
+    for (int n = 0; n < PF; n++) ring[n] = ld(n);
+#pragma unroll
+    for (int n = 0; n < N; n++) {
+      if (n + PF < N) ring[(n + PF) % (PF + 1)] = ld(n + PF);
+      sched_fence();
+      const int ks = n / C::ND, dn = n % C::ND;
+      acc[dn] = TT::mfma(pa[ks], ring[n % (PF + 1)], acc[dn]);
+      if (TT::SPLIT) acc[dn] = TT::mfma(pl[ks], ring[n % (PF + 1)], acc[dn]);
+    }
+  };
+  // Phase 1 for M = the step's queries, N = this wave's keys, A rows from `src` (same ring).
+  auto phase1 = [&](f16v *s, const short *src) {
+    constexpr int N = C::KK * C::MB, PF = ATTN_LDS_PREFETCH;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; mb++) s[mb] = f16v{};
+    auto ld = [&](int n) { return *(const s8v *)&src[nat_off(n % C::MB, n / C::MB)]; };
+    s8v ring[PF + 1];
+#pragma unroll
+    for (int n = 0; n < PF; n++) ring[n] = ld(n);
+#pragma unroll
+    for (int n = 0; n < N; n++) {
+      if (n + PF < N) ring[(n + PF) % (PF + 1)] = ld(n + PF);
+      sched_fence();
+      const int kk = n / C::MB, mb = n % C::MB;
+      s[mb] = TT::mfma(ring[n % (PF + 1)], kv[kk], s[mb]);
+    }
+  };
+  auto step_q0 = [&](int t) { return (qb_lo + t / p.G) * BN; };
+  auto step_full = [&](int q0) {
+    return (!p.causal || k0 + C::BM - 1 <= q0 + off) && (p.window <= 0 || k0 > q0 + BN - 1 + off - p.window) &&
+           (q0 + BN <= p.Sq) && (k0 + C::BM <= p.Skv);
+  };
+
+  if (nsteps > 0) issue(0, 0, 0);
   wait_vm0();
   __syncthreads();
 
-  for (int t = 0; t < nsteps; t++) {
-    const int buf = t & 1;
-    const int q0 = (qb_lo + t / p.G) * BN;
-    if (t + 1 < nsteps) issue(t + 1, buf ^ 1);
-    const bool full = (!p.causal || k0 + C::BM - 1 <= q0 + off) && (p.window <= 0 || k0 > q0 + BN - 1 + off - p.window) &&
-                      (q0 + BN <= p.Sq) && (k0 + C::BM <= p.Skv);
-    const short *qs = q_s[buf];
-    const short *dos = do_s[buf];
-
-    // Phase 1: S = Q K^T (P role) or dP = dO V^T (dS role); M = queries, N = this wave's keys.
-    f16v s[C::MB];
-#pragma unroll
-    for (int mb = 0; mb < C::MB; mb++) s[mb] = f16v{};
-    {
-      const short *asrc = role == 0 ? qs : dos;
-#pragma unroll
-      for (int kk = 0; kk < C::KK; kk++)
-#pragma unroll
-        for (int mb = 0; mb < C::MB; mb++) s[mb] = TT::mfma(*(const s8v *)&asrc[nat_off(mb, kk)], kv[kk], s[mb]);
-    }
-
-    // A operands of phase 2: P^T (P role) or dS^T (dS role), A[m=key][k=query], and their low
-    // halves when TT::SPLIT.  Register 8*(ks%2)+e of block ks/2 is query 16*ks + 8*(e/4) +
-    // 4*hi + e%4, matching the rows the transposed read below supplies.
-    s8v pa[C::KS], pl[C::KS];
-    auto pack = [&](int mb, int r, float x) {
-      const short xh = TT::cvt(x);
-      pa[2 * mb + (r >> 3)][r & 7] = xh;
-      pl[2 * mb + (r >> 3)][r & 7] = TT::SPLIT ? TT::cvt(x - TT::tof(xh)) : (short)0;
-    };
-    if (role == 0) {
+  if (role == 0) {
+    for (int t = 0; t < nsteps; t++) {
+      const int buf = t & 1;
+      const int q0 = step_q0(t);
+      if (t + 1 < nsteps) issue(t + 1, (t + 1) % 3, buf ^ 1);
+      f16v s[C::MB];
+      mfma_prio_hi();
+      phase1(s, q_s[t % 3]);
+      mfma_prio_lo();
+      s8v pa[C::KS], pl[C::KS];
       auto softmax = [&](auto masked) {
 #pragma unroll
         for (int mb = 0; mb < C::MB; mb++) {
@@ -177,20 +222,30 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
                 x = ((qi >= qlo) & (qi <= qhi)) ? x : 0.f;
               }
               pq[i] = x;
-              pack(mb, 4 * j + i, x);
+              pack(pa, pl, mb, 4 * j + i, x);
             }
             p_s[kgrp][mb][j][lane] = pq;
           }
         }
       };
-      if (full)
+      if (step_full(q0))
         softmax(std::false_type{});
       else
         softmax(std::true_type{});
+      __syncthreads();  // P visible to the dS-role waves
+      phase2(pa, pl, do_s[buf]);  // dV += P^T dO
+      wait_vm0();
+      __syncthreads();  // next tile landed; P and this step's dO consumed
     }
-    __syncthreads();  // P visible to the dS-role waves
-
-    if (role == 1) {
+  } else {
+    s8v da[C::KS], dl[C::KS];  // dS^T of the previous step
+    for (int t = 0; t < nsteps; t++) {
+      const int buf = t & 1;
+      if (t + 1 < nsteps) issue(t + 1, (t + 1) % 3, buf ^ 1);
+      if (t > 0) phase2(da, dl, q_s[(t + 2) % 3]);  // dK += dS^T Q of step t-1
+      f16v s[C::MB];
+      phase1(s, do_s[buf]);  // dP = dO V^T
+      __syncthreads();       // P of this step visible
 #pragma unroll
       for (int mb = 0; mb < C::MB; mb++)
 #pragma unroll
@@ -198,23 +253,12 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
           const f4v d4 = *(const f4v *)&dl_s[buf][32 * mb + 8 * j + 4 * hi];
           const f4v pq = p_s[kgrp][mb][j][lane];
 #pragma unroll
-          for (int i = 0; i < 4; i++) pack(mb, 4 * j + i, pq[i] * (s[mb][4 * j + i] - d4[i]));
+          for (int i = 0; i < 4; i++) pack(da, dl, mb, 4 * j + i, pq[i] * (s[mb][4 * j + i] - d4[i]));
         }
+      wait_vm0();
+      __syncthreads();  // next tile landed; P consumed
     }
-    // Phase 2: dV += P^T dO (P role) or dK += dS^T Q (dS role); B[k=query][n=d] transposed.
-    {
-      const short *bsrc = role == 0 ? dos : qs;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ks++)
-#pragma unroll
-        for (int dn = 0; dn < C::ND; dn++) {
-          const s8v bb = cat8(lds_tr4(&bsrc[tr_off(ks, dn, 0)]), lds_tr4(&bsrc[tr_off(ks, dn, 1)]));
-          acc[dn] = TT::mfma(pa[ks], bb, acc[dn]);
-          if (TT::SPLIT) acc[dn] = TT::mfma(pl[ks], bb, acc[dn]);
-        }
-    }
-    wait_vm0();
-    __syncthreads();  // next tile landed; P and this tile consumed
+    if (nsteps > 0) phase2(da, dl, q_s[(nsteps - 1) % 3]);
   }
 
   // Epilogue: dV (P role) or scale * dK (dS role), cast once, BSHD at the KV head.

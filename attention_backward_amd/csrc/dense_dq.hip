@@ -28,8 +28,13 @@
 
 namespace attn {
 
-template <int D, int BK>
+#ifndef ATTN_LDS_PREFETCH
+#define ATTN_LDS_PREFETCH 3
+#endif
+
+template <int D, int BK, int SB_ = 1>
 struct DqCfg {
+  static constexpr int SB = SB_;           // sub-blocks a tile is taken in
   static constexpr int NW = 8;             // waves per workgroup
   static constexpr int BQ = 32 * NW;       // query rows per workgroup
   static constexpr int KB = BK / 32;       // 32-key blocks per step
@@ -39,11 +44,12 @@ struct DqCfg {
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int WIW = BK * CPR / (64 * NW);  // 16-byte global->LDS loads per wave per tile
   static_assert(BK * CPR % (64 * NW) == 0, "tile must split evenly over the waves");
+  static_assert(KB % SB == 0, "sub-blocks of whole 32-key blocks");
 };
 
-template <class TT, int D, int BK>
+template <class TT, int D, int BK, int SB>
 __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
-  using C = DqCfg<D, BK>;
+  using C = DqCfg<D, BK, SB>;
   __shared__ __attribute__((aligned(16))) short k_s[2][BK * D];
   __shared__ __attribute__((aligned(16))) short v_s[2][BK * D];
 
@@ -136,50 +142,84 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
                         (k0 + BK <= p.Skv) && (qw0 + 32 <= p.Sq);
       const short *ks = k_s[buf];
       const short *vs = v_s[buf];
-      // S^T = K Q^T and dP^T = V dO^T: M = keys (KB blocks of 32), N = this wave's 32 queries.
-      f16v s[C::KB], dp[C::KB];
+      // The tile is taken as SB sub-blocks of KS = BK / SB keys, one after the other: each forms
+      // S^T = K Q^T and dP^T = V dO^T (M = keys in 32-row blocks, N = this wave's 32 queries), the
+      // softmax gradient, and dQ += dS K.  Fewer keys at a time hold fewer accumulators live.
 #pragma unroll
-      for (int kb = 0; kb < C::KB; kb++) s[kb] = dp[kb] = f16v{};
+      for (int sb = 0; sb < C::SB; sb++) {
+        constexpr int KBS = C::KB / C::SB, KSTS = C::KST / C::SB;
+        f16v s[KBS], dp[KBS];
 #pragma unroll
-      for (int kk = 0; kk < C::KK; kk++)
+        for (int kb = 0; kb < KBS; kb++) s[kb] = dp[kb] = f16v{};
+        mfma_prio_hi();
+        {
+          // K and V rows are read PF k-steps ahead through a ring of registers (the read
+          // latency hides behind the matrix core); the fences keep that order.
+          constexpr int N = C::KK * KBS, PF = ATTN_LDS_PREFETCH;
+          auto ldk = [&](int n) { return *(const s8v *)&ks[nat_off(sb * KBS + n % KBS, n / KBS)]; };
+          auto ldv = [&](int n) { return *(const s8v *)&vs[nat_off(sb * KBS + n % KBS, n / KBS)]; };
+          s8v rk[PF + 1], rv[PF + 1];
 #pragma unroll
-        for (int kb = 0; kb < C::KB; kb++) {
-          s[kb] = TT::mfma(*(const s8v *)&ks[nat_off(kb, kk)], qf[kk], s[kb]);
-          dp[kb] = TT::mfma(*(const s8v *)&vs[nat_off(kb, kk)], dof[kk], dp[kb]);
-        }
-      // P^T = exp2(S^T c - lse) (masked), dS^T = P^T (dP^T - delta).  dS feeds the next product
-      // as its A operand A[m=query][k=key]: registers 8*(kst%2)..+7 of block kst/2 cover keys
-      // 16*kst + 8*(e/4) + 4*hi + e%4, the rows the transposed read supplies.
-      s8v da[C::KST], dl[C::KST];
-      auto softmax_grad = [&](auto masked) {
-#pragma unroll
-        for (int kb = 0; kb < C::KB; kb++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) {
-            float x = exp2f_hw(s[kb][r] * p.c - lr);
-            if (decltype(masked)::value) {
-              const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-              x = ((kj >= klo) & (kj <= khi)) ? x : 0.f;
-            }
-            const float ds = x * (dp[kb][r] - dr);
-            const short dh = TT::cvt(ds);
-            da[2 * kb + (r >> 3)][r & 7] = dh;
-            dl[2 * kb + (r >> 3)][r & 7] = TT::SPLIT ? TT::cvt(ds - TT::tof(dh)) : (short)0;
+          for (int n = 0; n < PF; n++) {
+            rk[n] = ldk(n);
+            rv[n] = ldv(n);
           }
-      };
-      if (full)
-        softmax_grad(std::false_type{});
-      else
-        softmax_grad(std::true_type{});
-      // dQ += dS K: B = K[k=key][n=d] read transposed from LDS.
 #pragma unroll
-      for (int kst = 0; kst < C::KST; kst++)
-#pragma unroll
-        for (int dn = 0; dn < C::ND; dn++) {
-          const s8v bb = cat8(lds_tr4(&ks[tr_off(kst, dn, 0)]), lds_tr4(&ks[tr_off(kst, dn, 1)]));
-          acc[dn] = TT::mfma(da[kst], bb, acc[dn]);
-          if (TT::SPLIT) acc[dn] = TT::mfma(dl[kst], bb, acc[dn]);
+          for (int n = 0; n < N; n++) {
+            if (n + PF < N) {
+              rk[(n + PF) % (PF + 1)] = ldk(n + PF);
+              rv[(n + PF) % (PF + 1)] = ldv(n + PF);
+            }
+            sched_fence();
+            const int kk = n / KBS, kb = n % KBS;
+            s[kb] = TT::mfma(rk[n % (PF + 1)], qf[kk], s[kb]);
+            dp[kb] = TT::mfma(rv[n % (PF + 1)], dof[kk], dp[kb]);
+          }
         }
+        mfma_prio_lo();
+        s8v da[KSTS], dl[KSTS];
+        auto softmax_grad = [&](auto masked) {
+#pragma unroll
+          for (int kb = 0; kb < KBS; kb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+              float x = exp2f_hw(s[kb][r] * p.c - lr);
+              if (decltype(masked)::value) {
+                const int kj = k0 + 32 * (sb * KBS + kb) + 8 * (r >> 2) + 4 * hi + (r & 3);
+                x = ((kj >= klo) & (kj <= khi)) ? x : 0.f;
+              }
+              const float ds = x * (dp[kb][r] - dr);
+              const short dh = TT::cvt(ds);
+              da[2 * kb + (r >> 3)][r & 7] = dh;
+              dl[2 * kb + (r >> 3)][r & 7] = TT::SPLIT ? TT::cvt(ds - TT::tof(dh)) : (short)0;
+            }
+        };
+        if (full)
+          softmax_grad(std::false_type{});
+        else
+          softmax_grad(std::true_type{});
+        // dQ += dS K: B = K[k=key][n=d] read transposed from LDS, PF products ahead.
+        mfma_prio_hi();
+        {
+          constexpr int N = KSTS * C::ND, PF = ATTN_LDS_PREFETCH;
+          auto ld = [&](int n) {
+            const int kg = sb * KSTS + n / C::ND, dn = n % C::ND;
+            return cat8(lds_tr4(&ks[tr_off(kg, dn, 0)]), lds_tr4(&ks[tr_off(kg, dn, 1)]));
+          };
+          s8v ring[PF + 1];
+#pragma unroll
+          for (int n = 0; n < PF; n++) ring[n] = ld(n);
+#pragma unroll
+          for (int n = 0; n < N; n++) {
+            if (n + PF < N) ring[(n + PF) % (PF + 1)] = ld(n + PF);
+            sched_fence();
+            const int kst = n / C::ND, dn = n % C::ND;
+            acc[dn] = TT::mfma(da[kst], ring[n % (PF + 1)], acc[dn]);
+            if (TT::SPLIT) acc[dn] = TT::mfma(dl[kst], ring[n % (PF + 1)], acc[dn]);
+          }
+        }
+        mfma_prio_lo();
+      }
     }
     wait_vm0();
     __syncthreads();  // next tile landed; this tile consumed
@@ -197,19 +237,28 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   }
 }
 
-template <class TT, int D, int BK>
+template <class TT, int D, int BK, int SB>
 static hipError_t launch_dq_t(const Params &p, hipStream_t st) {
-  const int nqb = (p.Sq + DqCfg<D, BK>::BQ - 1) / DqCfg<D, BK>::BQ;
+  const int nqb = (p.Sq + DqCfg<D, BK, SB>::BQ - 1) / DqCfg<D, BK, SB>::BQ;
   const int64_t blocks = (int64_t)nqb * p.B * p.Hq;
   if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL((dense_dq_kernel<TT, D, BK>), dim3((unsigned)blocks), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((dense_dq_kernel<TT, D, BK, SB>), dim3((unsigned)blocks), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 
+#ifndef ATTN_DQ128_BK
+#define ATTN_DQ128_BK 64
+#endif
+#ifndef ATTN_DQ128_SB
+#define ATTN_DQ128_SB 2
+#endif
+
 hipError_t launch_dense_dq(const Params &p, bool bf16, hipStream_t st) {
-  // bf16 carries dS as two halves (hi + lo): at D = 128 it steps 32 keys to stay within 256 VGPRs.
-  if (p.Dqk == 128) return bf16 ? launch_dq_t<BF16, 128, 32>(p, st) : launch_dq_t<F16, 128, 64>(p, st);
-  if (p.Dqk == 64) return bf16 ? launch_dq_t<BF16, 64, 64>(p, st) : launch_dq_t<F16, 64, 64>(p, st);
+  // At D = 128, 64-key tiles are taken as two 32-key sub-blocks, so that the S/dP accumulators of
+  // one sub-block (and, for bf16, dS as hi + lo halves) fit in 256 VGPRs without spilling.
+  constexpr int BK = ATTN_DQ128_BK, SB = ATTN_DQ128_SB;
+  if (p.Dqk == 128) return bf16 ? launch_dq_t<BF16, 128, BK, SB>(p, st) : launch_dq_t<F16, 128, BK, SB>(p, st);
+  if (p.Dqk == 64) return bf16 ? launch_dq_t<BF16, 64, 64, 1>(p, st) : launch_dq_t<F16, 64, 64, 1>(p, st);
   return hipErrorInvalidValue;
 }
 
