@@ -37,11 +37,22 @@ CFLAGS = [
     "-I", INCLUDE,
     "-I", CSRC,
 ]
+# Kernels that run one wave per SIMD (up to 512 registers) keep their accumulators in AGPRs, where
+# the MFMAs read and write them directly; the VGPR form would park them there anyway and copy
+# them back and forth every step.
+AGPR_FORM = {"sparse_dkdv.hip", "sparse_bwd.hip"}
+
+
+def _flags(src: str):
+    if os.path.basename(src) not in AGPR_FORM:
+        return CFLAGS
+    i = CFLAGS.index("-amdgpu-mfma-vgpr-form=1")
+    return CFLAGS[: i - 1] + CFLAGS[i + 1:]
 
 
 def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
+    cmd = [HIPCC, *_flags(src), *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -3,8 +3,9 @@
 // Validates every argument on the host before anything is enqueued, carves the workspace,
 // and enqueues the kernels on the caller's stream:
 //   dense:  delta (preprocess) -> dK/dV (KV-block owned) -> dQ (query-block owned)
-//   top-k:  zero the f32 dK/dV accumulators, delta -> gathered backward (dQ owned, dK/dV
-//           added into the accumulators) -> landing (scale, cast).
+//   top-k:  zero the f32 dK/dV accumulators and the key-count mask, delta, count the keys of
+//           every list -> gathered dQ (query-owned) -> dK/dV (key-owned, weighted by the
+//           counts, added into the accumulators) -> landing (scale, cast).
 // The library keeps no state between calls.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -43,7 +44,7 @@ int validate_sizes(const attn_bwd_args *a) {
   const int64_t lim = (int64_t)1 << 31;
   if (a->B * a->Sq * a->Hq >= lim || a->B * a->Skv * a->Hkv >= lim) return ATTN_E_UNSUPPORTED;
   if (a->topk_idx) {
-    if (a->topk >= lim) return ATTN_E_UNSUPPORTED;
+    if (a->topk > 65535) return ATTN_E_UNSUPPORTED;  // 16-bit key counts
     if (!(a->Dqk == 576 && a->Dv == 512)) return ATTN_E_UNSUPPORTED;
   } else if (!((a->Dqk == 64 && a->Dv == 64) || (a->Dqk == 128 && a->Dv == 128))) {
     return ATTN_E_UNSUPPORTED;
@@ -52,13 +53,16 @@ int validate_sizes(const attn_bwd_args *a) {
 }
 
 // Workspace, each part 256-byte aligned: delta [B,Hq,Sq] f32, the sanitised lse [B,Hq,Sq] f32,
-// and for the top-k path the accumulators dK_acc [B,Skv,Hkv,Dqk] and dV_acc [B,Skv,Hkv,Dv] f32.
+// and for the top-k path the accumulators dK_acc [B,Skv,Hkv,Dqk] and dV_acc [B,Skv,Hkv,Dv] f32
+// and the key counts cnt [B,Hkv,Sq,skv_pad] u16 (skv_pad = Skv rounded up to 32).
 size_t row_stat_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Hq * a->Sq) * sizeof(float)); }
 size_t dk_acc_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Skv * a->Hkv * a->Dqk) * 4); }
 size_t dv_acc_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Skv * a->Hkv * a->Dv) * 4); }
+int64_t skv_pad(const attn_bwd_args *a) { return (a->Skv + 31) / 32 * 32; }
+size_t cnt_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Hkv * a->Sq * skv_pad(a)) * 2); }
 size_t workspace_bytes_for(const attn_bwd_args *a) {
   size_t n = 2 * row_stat_bytes(a);
-  if (a->topk_idx) n += dk_acc_bytes(a) + dv_acc_bytes(a);
+  if (a->topk_idx) n += dk_acc_bytes(a) + dv_acc_bytes(a) + cnt_bytes(a);
   return n;
 }
 
@@ -133,10 +137,16 @@ int attn_bwd_ex(const attn_bwd_args *a) {
   } else {
     float *dk_acc = (float *)((char *)ws + 2 * row_stat_bytes(a));
     float *dv_acc = (float *)((char *)dk_acc + dk_acc_bytes(a));
+    uint16_t *cnt = (uint16_t *)((char *)dv_acc + dv_acc_bytes(a));
     const int64_t nk = a->B * a->Skv * a->Hkv * a->Dqk, nv = a->B * a->Skv * a->Hkv * a->Dv;
-    if (e == hipSuccess) e = attn::launch_zero(dk_acc, (int64_t)((dk_acc_bytes(a) + dv_acc_bytes(a)) / 4), st);
+    const size_t zero_bytes = dk_acc_bytes(a) + dv_acc_bytes(a) + cnt_bytes(a);  // contiguous
+    if (e == hipSuccess) e = attn::launch_zero(dk_acc, (int64_t)(zero_bytes / 4), st);
+    if (e == hipSuccess)
+      e = attn::launch_topk_count(a->topk_idx, cnt, a->B, a->Sq, a->Skv, a->Hkv, a->topk, (int)skv_pad(a), a->causal,
+                                  st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-    if (e == hipSuccess) e = attn::launch_sparse_bwd(p, dk_acc, dv_acc, bf16, st);
+    if (e == hipSuccess) e = attn::launch_sparse_dq(p, bf16, st);
+    if (e == hipSuccess) e = attn::launch_sparse_dkdv(p, cnt, (int)skv_pad(a), dk_acc, dv_acc, bf16, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
     if (e == hipSuccess) e = attn::launch_land(dk_acc, p.dk, nk, a->scale, bf16, st);
     if (e == hipSuccess) e = attn::launch_land(dv_acc, p.dv, nv, 1.0f, bf16, st);

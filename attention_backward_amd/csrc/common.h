@@ -107,6 +107,22 @@ __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" :
 // sinks such reads next to their use to save registers, which exposes the LDS latency).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Software pipeline over N operand loads: ld(n) is issued PF uses ahead of use(n, value), through
+// a ring of PF + 1 registers; the fences keep the compiler from sinking the loads to their uses.
+template <int N, int PF, class Ld, class Use>
+__device__ __forceinline__ void ring_pipeline(Ld ld, Use use) {
+  using T = decltype(ld(0));
+  T ring[PF + 1];
+#pragma unroll
+  for (int n = 0; n < PF && n < N; n++) ring[n] = ld(n);
+#pragma unroll
+  for (int n = 0; n < N; n++) {
+    if (n + PF < N) ring[(n + PF) % (PF + 1)] = ld(n + PF);
+    sched_fence();
+    use(n, ring[n % (PF + 1)]);
+  }
+}
+
 // Wave priority around MFMA sections (a scheduling hint between the waves sharing a SIMD: the
 // wave feeding the matrix core issues first, its partner's vector work fills the gaps).
 #ifndef ATTN_MFMA_PRIO

@@ -16,11 +16,19 @@ hipError_t launch_delta(const short *o, const short *dout, float *delta, const f
 hipError_t launch_dense_dkdv(const Params &p, bool bf16, hipStream_t st);
 hipError_t launch_dense_dq(const Params &p, bool bf16, hipStream_t st);
 
-// Top-k path, (Dqk, Dv) = (576, 512): gathered backward adding dK/dV into f32 accumulators
-// [B,Skv,Hkv,Dqk] / [B,Skv,Hkv,Dv] (zeroed first by launch_zero), then the landing pass
-// out = storage(scale * acc) over n elements (n a multiple of 8).
+// Top-k path, (Dqk, Dv) = (576, 512):
+//   launch_zero        zero-fills n floats (n a multiple of 4): the accumulators and count mask;
+//   launch_topk_count  cnt [B,Hkv,Sq,skv_pad] u16 = occurrences of each key in each valid list;
+//   launch_sparse_dq   gathered, query-owned dQ;
+//   launch_sparse_dkdv key-owned dK/dV weighted by cnt, added into f32 accumulators
+//                      [B,Skv,Hkv,Dqk] / [B,Skv,Hkv,Dv];
+//   launch_land        out = storage(scale * acc) over n elements (n a multiple of 8).
 hipError_t launch_zero(float *buf, int64_t n, hipStream_t st);
-hipError_t launch_sparse_bwd(const Params &p, float *dk_acc, float *dv_acc, bool bf16, hipStream_t st);
+hipError_t launch_topk_count(const int32_t *idx, uint16_t *cnt, int64_t B, int64_t Sq, int64_t Skv, int64_t Hkv,
+                             int64_t topk, int skv_pad, int causal, hipStream_t st);
+hipError_t launch_sparse_dq(const Params &p, bool bf16, hipStream_t st);
+hipError_t launch_sparse_dkdv(const Params &p, const uint16_t *cnt, int skv_pad, float *dk_acc, float *dv_acc, bool bf16,
+                              hipStream_t st);
 hipError_t launch_land(const float *acc, short *out, int64_t n, float scale, bool bf16, hipStream_t st);
 
 }  // namespace attn

@@ -1,24 +1,23 @@
-// sparse_bwd.hip -- backward of attention over a gathered top-k key set per query.
+// sparse_bwd.hip -- dQ of the top-k backward: gathered, query-owned; and the f32 accumulator
+// zero-fill and landing passes of the top-k path.
 //
-// TileLang PR #2592 page (sparse MLA backward): each query row attends to its own list of
-// top-k keys, shared by all query heads of a KV head; gradients for the shape H = 64 query
-// heads, one KV head, Dqk = 576, Dv = 512, topk = 2048.  The page describes the kernel as
-// bound by the gather of K/V rows ("memory-pipe bound"), whose latency is hidden by having
-// many loads in flight.
+// TileLang PR #2592 page (sparse MLA backward): each query row attends to its own list of top-k
+// keys, shared by all query heads of a KV head; the shape there is H = 64 query heads, one KV
+// head, Dqk = 576, Dv = 512, topk = 2048.  The page finds the kernel bound by the gather of K/V
+// rows, hidden only by keeping many loads in flight.
 //
-// Kernel (gfx950): one workgroup (4 wave64s) per (batch, query row, KV head, block of 32 query
-// heads).  The query block's Q and dO rows sit in LDS for the whole workgroup; the query's key
+// dQ kernel (gfx950): one workgroup (4 wave64s, one per SIMD) per (batch, query row, KV head, block
+// of 32 query heads).  Waves 0-1 hold the block's Q rows (each half of Dqk) and waves 2-3 its dO
+// rows (each half of Dv) in registers as MFMA A operands for the whole walk.  The query's key
 // list is walked in chunks of 32 slots whose K and V rows are gathered straight into LDS by
-// direct global->LDS loads (the gather is the hot memory path; 32 rows x (Dqk + Dv) per chunk
-// are in flight at once).  Per chunk, on 32x32x16 MFMA with f32 accumulation:
-//   S = Q K^T and dP = dO V^T   (split over the head dim: waves 0-1 form S, 2-3 form dP),
-//   P = exp2(S*c - lse), dS = P (dP - delta)   (masked slots: padding -1, out of range or
-//                                               past the causal diagonal contribute nothing),
-//   dQ += dS K                  (owned by the workgroup, kept in registers, written once),
-//   dK[idx] += dS^T Q, dV[idx] += P^T dO   (summed over the 32 heads by the MFMA itself, then
-//                                           added with f32 atomics into accumulators at Hkv
-//                                           heads; a landing pass scales and casts them).
-// Each list entry counts once per occurrence, as the index list defines the multiset of keys.
+// direct global->LDS loads, double-buffered so that chunk c+1 is in flight while chunk c is
+// computed.  Per chunk, on MFMA with f32 accumulation:
+//   S = Q K^T and dP = dO V^T   (partial sums over the halves of the head dims, summed in LDS),
+//   P = exp2(S*c - lse), dS = P (dP - delta)   (masked slots: padding -1, out of range or past
+//                                               the causal diagonal contribute nothing),
+//   dQ += dS K                  (owned by the workgroup, kept in registers, written once).
+// Each list entry counts once per occurrence.  dK and dV come from the key-owned pass in
+// sparse_dkdv.hip.
 #include "common.h"
 #include "kernels.h"
 
@@ -53,21 +52,18 @@ __device__ __forceinline__ int sp_sw(int row) {
 }
 
 template <class TT, int DQK, int DV>
-__global__ __launch_bounds__(256, 1) void sparse_bwd_kernel(const Params p, float *__restrict__ dk_acc,
-                                                            float *__restrict__ dv_acc) {
+__global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
   using C = SpCfg<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) short q_s[C::HB * DQK];
-  __shared__ __attribute__((aligned(16))) short do_s[C::HB * DV];
-  __shared__ __attribute__((aligned(16))) short k_s[C::KC * DQK];
-  __shared__ __attribute__((aligned(16))) short v_s[C::KC * DV];
-  __shared__ __attribute__((aligned(16))) float part_s[4][16][64];  // S/dP partials; later P/dS
-  __shared__ int idx_s[C::KC];   // key of each slot, -1 where the slot is masked
-  __shared__ int row_s[C::KC];   // row gathered for each slot (a valid key of the chunk)
-  __shared__ int any_s;          // whether the chunk has a valid slot
-  __shared__ float lse_s[C::HB], dl_s[C::HB];
-  // P and dS as 16-bit [head][slot] tiles (hi, then lo halves for bf16) alias part_s.
-  short *st_p = (short *)&part_s[0][0][0];  // [2][HB][KC]
-  short *st_ds = st_p + 2 * C::HB * C::KC;   // [2][HB][KC]
+  constexpr int PF = 3;
+  __shared__ __attribute__((aligned(16))) short k_s[2][C::KC * DQK];
+  __shared__ __attribute__((aligned(16))) short v_s[2][C::KC * DV];
+  __shared__ __attribute__((aligned(16))) float part_s[4][16][64];  // S/dP partials
+  __shared__ __attribute__((aligned(16))) short st_ds[2][C::HB * C::KC];  // dS [head][slot], hi / lo
+  // Slot lists of chunks c, c+1 and c+2 (three buffers: the list of c+2 is written while chunk c
+  // is still being read).
+  __shared__ int idx_s[3][C::KC];  // key of each slot, -1 where the slot is masked
+  __shared__ int row_s[3][C::KC];  // row gathered for each slot (a valid key of the chunk)
+  __shared__ int any_s[3];         // whether the chunk has a valid slot
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -86,22 +82,29 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_kernel(const Params p, floa
   const int off = p.Skv - p.Sq;
   const int64_t qrow = ((int64_t)b * p.Sq + i) * p.Hq;  // + h: BSHD row of (b, i, h)
 
-  // Q and dO rows of the block's heads (rows past nh repeat head nh-1; they are masked below).
-  for (int s = tid; s < C::HB * C::CQ; s += 256) {
-    const int r = s / C::CQ, ch = (s % C::CQ) ^ sp_sw<DQK>(r);
-    const int h = h0 + min(r, nh - 1);
-    g2lds16(p.q + (qrow + h) * DQK + 8 * ch, &q_s[(s - lane) * 8]);
+  // Resident A operands A[m = head lo][k = d] (32x32x16 layout): waves 0-1 Q rows over their half
+  // of Dqk, waves 2-3 dO rows over their half of Dv.  Rows past nh repeat head nh-1 (masked).
+  const bool sw_ = w < 2;
+  constexpr int KH = (C::KQ / 2 > C::KV / 2) ? C::KQ / 2 : C::KV / 2;
+  const int nk = sw_ ? C::KQ / 2 : C::KV / 2;
+  const int k0 = (w & 1) * nk;
+  s8v ar[KH];
+  {
+    const int64_t r = qrow + h0 + min(lo, nh - 1);
+#pragma unroll
+    for (int u = 0; u < KH; u++) {
+      const int kk = k0 + min(u, nk - 1);
+      ar[u] = sw_ ? *(const s8v *)(p.q + r * DQK + 16 * kk + 8 * hi) : *(const s8v *)(p.dout + r * DV + 16 * kk + 8 * hi);
+    }
   }
-  for (int s = tid; s < C::HB * C::CV; s += 256) {
-    const int r = s / C::CV, ch = (s % C::CV) ^ sp_sw<DV>(r);
-    const int h = h0 + min(r, nh - 1);
-    g2lds16(p.dout + (qrow + h) * DV + 8 * ch, &do_s[(s - lane) * 8]);
-  }
-  if (tid < C::HB) {
-    const int h = h0 + min(tid, nh - 1);
-    const int64_t li = ((int64_t)b * p.Hq + h) * p.Sq + i;
-    lse_s[tid] = p.lse[li];
-    dl_s[tid] = p.delta[li];
+  // lse and delta of the lane's rows of the accumulator layout (row m = 8*(r/4) + 4*hi + r%4).
+  float lse_r[16], dl_r[16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    const int m = min(8 * (r >> 2) + 4 * hi + (r & 3), nh - 1);
+    const int64_t li = ((int64_t)b * p.Hq + h0 + m) * p.Sq + i;
+    lse_r[r] = p.lse[li];
+    dl_r[r] = p.delta[li];
   }
 
   // dQ accumulators: this wave owns the 32-wide d-blocks w, w+4, ... for the whole walk.
@@ -113,170 +116,147 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_kernel(const Params p, floa
   const int32_t *idx_row = p.idx + (((int64_t)b * p.Sq + i) * p.Hkv + g) * p.topk;
   const int nchunks = (p.topk + C::KC - 1) / C::KC;
 
-  for (int cidx = 0; cidx < nchunks; cidx++) {
-    const int t0 = cidx * C::KC;
-    __syncthreads();  // the previous chunk is fully consumed (k_s, v_s, idx_s, staging)
-    if (w == 0) {
-      // Slots are lanes 0..KC-1 of wave 0.  A masked slot (padding, out of range, past the
-      // causal diagonal) gathers the row of the chunk's first valid slot, so every row in the
-      // tile is one this query attends; its own P and dS are forced to zero.
-      int j = -1;
-      if (lane < C::KC) {
-        const int t = t0 + lane;
-        j = t < p.topk ? idx_row[t] : -1;
-        if (j < 0 || j >= p.Skv || (p.causal && j > i + off)) j = -1;
-      }
-      const uint64_t m = __ballot(j >= 0);
-      const int first = m ? __shfl(j, __builtin_ctzll(m)) : 0;
-      if (lane < C::KC) {
-        idx_s[lane] = j;
-        row_s[lane] = j >= 0 ? j : first;
-      }
-      if (lane == 0) any_s = m != 0;
+  // Slots of chunk c (wave 0): a masked slot (padding, out of range, past the causal diagonal)
+  // gathers the row of the chunk's first valid slot, so every gathered row is one this query
+  // attends; its own P and dS are forced to zero.
+  auto slots = [&](int c) {
+    const int buf = c % 3;
+    int j = -1;
+    if (lane < C::KC) {
+      const int t = c * C::KC + lane;
+      j = t < p.topk ? idx_row[t] : -1;
+      if (j < 0 || j >= p.Skv || (p.causal && j > i + off)) j = -1;
     }
-    __syncthreads();
-    if (!any_s) continue;  // uniform: nothing in this chunk contributes
-    for (int s = tid; s < C::KC * C::CQ; s += 256) {
-      const int r = s / C::CQ, ch = (s % C::CQ) ^ sp_sw<DQK>(r);
-      g2lds16(p.k + (((int64_t)b * p.Skv + row_s[r]) * p.Hkv + g) * DQK + 8 * ch, &k_s[(s - lane) * 8]);
+    const uint64_t m = __ballot(j >= 0);
+    const int first = m ? __shfl(j, __builtin_ctzll(m)) : 0;
+    if (lane < C::KC) {
+      idx_s[buf][lane] = j;
+      row_s[buf][lane] = j >= 0 ? j : first;
     }
-    for (int s = tid; s < C::KC * C::CV; s += 256) {
-      const int r = s / C::CV, ch = (s % C::CV) ^ sp_sw<DV>(r);
-      g2lds16(p.v + (((int64_t)b * p.Skv + row_s[r]) * p.Hkv + g) * DV + 8 * ch, &v_s[(s - lane) * 8]);
+    if (lane == 0) any_s[buf] = m != 0;
+  };
+  auto gather = [&](int c) {
+    const int buf = c & 1, sb = c % 3;
+#pragma unroll
+    for (int u = 0; u < C::KC * C::CQ / 256; u++) {
+      const int s = 256 * u + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sp_sw<DQK>(r);
+      g2lds16(p.k + (((int64_t)b * p.Skv + row_s[sb][r]) * p.Hkv + g) * DQK + 8 * ch, &k_s[buf][(s - lane) * 8]);
     }
-    wait_vm0();
-    __syncthreads();
+    if (C::KC * C::CQ % 256 != 0 && tid < C::KC * C::CQ % 256) {
+      const int s = C::KC * C::CQ / 256 * 256 + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sp_sw<DQK>(r);
+      g2lds16(p.k + (((int64_t)b * p.Skv + row_s[sb][r]) * p.Hkv + g) * DQK + 8 * ch, &k_s[buf][(s - lane) * 8]);
+    }
+#pragma unroll
+    for (int u = 0; u < C::KC * C::CV / 256; u++) {
+      const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sp_sw<DV>(r);
+      g2lds16(p.v + (((int64_t)b * p.Skv + row_s[sb][r]) * p.Hkv + g) * DV + 8 * ch, &v_s[buf][(s - lane) * 8]);
+    }
+  };
+  // B[k][n] = tile[row = 16*ks + 8*hi + e][col = 32*nb + lo] by transposed reads of a row-major
+  // [slot][d] tile: per 16-lane group, lanes 4r..4r+3 supply 16 columns of row r and lane i
+  // receives column i of the 4 rows.
+  auto trB = [&](const short *tile, int ks, int nb) {
+    const int col = 32 * nb + 16 * (g16 & 1) + 4 * (i16 & 3);
+    s4v part[2];
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+      const int row = 16 * ks + 8 * hi + 4 * half + (i16 >> 2);
+      const int ch = (col >> 3) ^ sp_sw<DQK>(row);
+      part[half] = lds_tr4(&tile[row * DQK + 8 * ch + (col & 7)]);
+    }
+    return cat8(part[0], part[1]);
+  };
 
-    // Phase A: S (waves 0, 1: halves of Dqk) and dP (waves 2, 3: halves of Dv); M = heads,
-    // N = key slots; A = Q / dO rows and B = K / V rows, both natural b128 reads.
+  if (w == 0) slots(0);
+  __syncthreads();
+  gather(0);
+  if (w == 0 && nchunks > 1) slots(1);
+  wait_vm0();
+  __syncthreads();
+
+  for (int c = 0; c < nchunks; c++) {
+    const int buf = c & 1, sb = c % 3;
+    if (c + 1 < nchunks) gather(c + 1);  // rows of chunk c+1 became visible at the last barrier
+
+    // Phase A: partial S (waves 0-1) or dP (waves 2-3) over this wave's half of the head dim;
+    // M = heads, N = slots.  B = K / V rows of the slots, natural reads through a ring; two
+    // accumulators so that consecutive products are independent.
     {
-      f16v acc = f16v{};
-      if (w < 2) {
-        const int sw = sp_sw<DQK>(lo);
-        for (int kk = w * (C::KQ / 2); kk < (w + 1) * (C::KQ / 2); kk++) {
-          const int ch = (2 * kk + hi) ^ sw;
-          acc = TT::mfma(*(const s8v *)&q_s[lo * DQK + 8 * ch], *(const s8v *)&k_s[lo * DQK + 8 * ch], acc);
-        }
-      } else {
-        const int sw = sp_sw<DV>(lo);
-        for (int kk = (w - 2) * (C::KV / 2); kk < (w - 1) * (C::KV / 2); kk++) {
-          const int ch = (2 * kk + hi) ^ sw;
-          acc = TT::mfma(*(const s8v *)&do_s[lo * DV + 8 * ch], *(const s8v *)&v_s[lo * DV + 8 * ch], acc);
-        }
-      }
+      const short *bt = sw_ ? k_s[buf] : v_s[buf];
+      const int rowlen = sw_ ? DQK : DV;
+      const int sw = sw_ ? sp_sw<DQK>(lo) : sp_sw<DV>(lo);
+      f16v a0 = f16v{}, a1 = f16v{};
+      ring_pipeline<KH, PF>(
+          [&](int u) {
+            const int kk = k0 + min(u, nk - 1);
+            return *(const s8v *)&bt[lo * rowlen + 8 * ((2 * kk + hi) ^ sw)];
+          },
+          [&](int u, s8v bv) {
+            if (u < nk) {
+              if (u & 1)
+                a1 = TT::mfma(ar[u], bv, a1);
+              else
+                a0 = TT::mfma(ar[u], bv, a0);
+            }
+          });
 #pragma unroll
-      for (int r = 0; r < 16; r++) part_s[w][r][lane] = acc[r];
+      for (int r = 0; r < 16; r++) part_s[w][r][lane] = a0[r] + a1[r];
     }
-    __syncthreads();
-    // Phase B: P and dS in the accumulator layout (row m = head 8*(r/4) + 4*hi + r%4, column =
-    // slot lo).  Formed by wave 0 only; padded head rows (m >= nh) and masked slots give 0.
-    if (w == 0) {
-      const bool slot_ok = idx_s[lo] >= 0;
-      float pv[16], dsv[16];
+    __syncthreads();  // partials visible
+    // Phase B: dS for accumulator registers r = 4w..4w+3 (row m = head 8*(r/4) + 4*hi + r%4,
+    // column = slot lo); padded head rows and masked slots give 0.
+    {
+      const bool slot_ok = idx_s[sb][lo] >= 0;
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
+      for (int q = 0; q < 4; q++) {
+        const int r = 4 * w + q;
         const int m = 8 * (r >> 2) + 4 * hi + (r & 3);
         const float sv = part_s[0][r][lane] + part_s[1][r][lane];
         const float dpv = part_s[2][r][lane] + part_s[3][r][lane];
         const bool ok = slot_ok && m < nh;
-        const float pr = exp2f_hw(sv * p.c - lse_s[m]);
-        pv[r] = ok ? pr : 0.f;
-        dsv[r] = ok ? pr * (dpv - dl_s[m]) : 0.f;
-      }
-      // The staging tiles alias part_s; this wave's reads of it above are complete before its
-      // writes below (one wave's LDS instructions execute in order), and no other wave reads
-      // part_s in this phase.
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int m = 8 * (r >> 2) + 4 * hi + (r & 3);
-        const short ph = TT::cvt(pv[r]), dh = TT::cvt(dsv[r]);
-        st_p[m * C::KC + lo] = ph;
-        st_ds[m * C::KC + lo] = dh;
-        st_p[C::HB * C::KC + m * C::KC + lo] = TT::SPLIT ? TT::cvt(pv[r] - TT::tof(ph)) : (short)0;
-        st_ds[C::HB * C::KC + m * C::KC + lo] = TT::SPLIT ? TT::cvt(dsv[r] - TT::tof(dh)) : (short)0;
+        const float pr = exp2f_hw(sv * p.c - lse_r[r]);
+        const float ds = ok ? pr * (dpv - dl_r[r]) : 0.f;
+        const short dh = TT::cvt(ds);
+        st_ds[0][m * C::KC + lo] = dh;
+        if (TT::SPLIT) st_ds[1][m * C::KC + lo] = TT::cvt(ds - TT::tof(dh));
       }
     }
-    __syncthreads();
-
-    // Phase C.  B operands B[k][n] = tile[row = 16*ks + 8*hi + e][col = 32*nb + lo] come from
-    // the row-major Q, dO and K tiles by transposed reads: per 16-lane group, lanes 4r..4r+3
-    // supply 16 columns of row r and lane i receives column i of the 4 rows, so the group
-    // 16*(g16&1) + i16 = lo gets its own column and two reads (+4 rows) give the 8 k values.
-    auto trB = [&](const short *tile, bool is_q, int ks, int nb) {
-      const int rowlen = is_q ? DQK : DV;
-      const int col = 32 * nb + 16 * (g16 & 1) + 4 * (i16 & 3);
-      s4v part[2];
-#pragma unroll
-      for (int half = 0; half < 2; half++) {
-        const int row = 16 * ks + 8 * hi + 4 * half + (i16 >> 2);
-        const int ch = (col >> 3) ^ (is_q ? sp_sw<DQK>(row) : sp_sw<DV>(row));
-        part[half] = lds_tr4(&tile[row * rowlen + 8 * ch + (col & 7)]);
-      }
-      return cat8(part[0], part[1]);
-    };
-    // A operand of dQ: dS[m = head lo][k = key slots 16*ks + 8*hi + e], natural read.
-    auto dsA = [&](int ks, int lohalf) {
-      return *(const s8v *)&st_ds[lohalf * C::HB * C::KC + lo * C::KC + 16 * ks + 8 * hi];
-    };
-    // A operand of dK/dV: X^T[m = key slot lo][k = heads 16*ks + 8*hi + e] from the [head][key]
-    // staging tile by transposed reads (4 heads per read).
-    auto stT = [&](const short *tile, int ks, int lohalf) {
-      const short *t = tile + lohalf * C::HB * C::KC;
-      s4v part[2];
-#pragma unroll
-      for (int half = 0; half < 2; half++) {
-        const int row = 16 * ks + 8 * hi + 4 * half + (i16 >> 2);
-        const int col = 16 * (g16 & 1) + 4 * (i16 & 3);
-        part[half] = lds_tr4(&t[row * C::KC + col]);
-      }
-      return cat8(part[0], part[1]);
-    };
-
-    // dQ += dS K  (this wave's d-blocks)
-#pragma unroll
-    for (int u = 0; u < NQW; u++) {
-      const int nb = w + 4 * u;
-      if (nb < C::NQ) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-          const s8v bb = trB(k_s, true, ks, nb);
-          dq[u] = TT::mfma(dsA(ks, 0), bb, dq[u]);
-          if (TT::SPLIT) dq[u] = TT::mfma(dsA(ks, 1), bb, dq[u]);
-        }
-      }
-    }
-    // dK[idx] += dS^T Q and dV[idx] += P^T dO, one 32x32 block at a time, added atomically.
-    auto scatter = [&](float *accbuf, int dlen, int nb, const f16v &c) {
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int slot = 8 * (r >> 2) + 4 * hi + (r & 3);
-        const int j = idx_s[slot];
-        if (j >= 0) unsafeAtomicAdd(&accbuf[(((int64_t)b * p.Skv + j) * p.Hkv + g) * dlen + 32 * nb + lo], c[r]);
-      }
-    };
-    for (int nb = w; nb < C::NQ; nb += 4) {
-      f16v c = f16v{};
+    if (w == 0 && c + 2 < nchunks) slots(c + 2);  // read after the next barrier
+    __syncthreads();  // dS visible
+    // Phase C: dQ += dS K for this wave's d-blocks; A = dS[m = head lo][k = slots 16*ks + 8*hi
+    // + e] (natural read), B = K^T by transposed reads through a ring.  A chunk with no valid
+    // slot contributes nothing and is skipped (its gathered rows are not this query's keys).
+    if (any_s[sb]) {
+      s8v da[2], dl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ks++) {
-        const s8v bb = trB(q_s, true, ks, nb);
-        c = TT::mfma(stT(st_ds, ks, 0), bb, c);
-        if (TT::SPLIT) c = TT::mfma(stT(st_ds, ks, 1), bb, c);
+        da[ks] = *(const s8v *)&st_ds[0][lo * C::KC + 16 * ks + 8 * hi];
+        dl[ks] = TT::SPLIT ? *(const s8v *)&st_ds[1][lo * C::KC + 16 * ks + 8 * hi] : s8v{};
       }
-      scatter(dk_acc, DQK, nb, c);
+      constexpr int N = 2 * NQW;
+      s8v prev_b = s8v{};
+      int prev_n = -1;
+      auto lo_product = [&](int n, s8v bb) {
+        const int ks = n / NQW, u = n % NQW;
+        if (w + 4 * u < C::NQ) dq[u] = TT::mfma(dl[ks], bb, dq[u]);
+      };
+      ring_pipeline<N, PF>(
+          [&](int n) { return trB(k_s[buf], n / NQW, min(w + 4 * (n % NQW), C::NQ - 1)); },
+          [&](int n, s8v bb) {
+            const int ks = n / NQW, u = n % NQW;
+            if (w + 4 * u < C::NQ) dq[u] = TT::mfma(da[ks], bb, dq[u]);
+            if (TT::SPLIT) {
+              if (prev_n >= 0) lo_product(prev_n, prev_b);
+              prev_n = n;
+              prev_b = bb;
+            }
+          });
+      if (TT::SPLIT) lo_product(prev_n, prev_b);
     }
-    for (int nb = w; nb < C::NV; nb += 4) {
-      f16v c = f16v{};
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
-        const s8v bb = trB(do_s, false, ks, nb);
-        c = TT::mfma(stT(st_p, ks, 0), bb, c);
-        if (TT::SPLIT) c = TT::mfma(stT(st_p, ks, 1), bb, c);
-      }
-      scatter(dv_acc, DV, nb, c);
-    }
+    wait_vm0();
+    __syncthreads();  // chunk c+1 landed, its rows' successor visible; chunk c consumed
   }
 
-  wait_vm0();  // the Q/dO loads, when every chunk was skipped
   // dQ = scale * acc for the block's valid heads (row m = head, column = d).
 #pragma unroll
   for (int u = 0; u < NQW; u++) {
@@ -323,15 +303,15 @@ hipError_t launch_zero(float *buf, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_bwd(const Params &p, float *dk_acc, float *dv_acc, bool bf16, hipStream_t st) {
+hipError_t launch_sparse_dq(const Params &p, bool bf16, hipStream_t st) {
   if (p.Dqk != 576 || p.Dv != 512) return hipErrorInvalidValue;
   const int nhb = (p.G + SpCfg<576, 512>::HB - 1) / SpCfg<576, 512>::HB;
   const int64_t blocks = (int64_t)p.B * p.Sq * p.Hkv * nhb;
   if (blocks < 1) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL((sparse_bwd_kernel<BF16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p, dk_acc, dv_acc);
+    hipLaunchKernelGGL((sparse_dq_kernel<BF16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((sparse_bwd_kernel<F16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p, dk_acc, dv_acc);
+    hipLaunchKernelGGL((sparse_dq_kernel<F16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

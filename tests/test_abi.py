@@ -44,9 +44,12 @@ def test_workspace_size():
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=4)) == 2 * (2 * 32 * 2048 * 4)
     assert ab.attn_bwd_workspace_size(valid_args(B=1, Sq=3, Hq=2, Hkv=2)) == 512  # 256-byte granularity
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=5)) == 0
-    # top-k: delta and lse rows, then f32 dK/dV accumulators at Hkv
+    # top-k: delta and lse rows, f32 dK/dV accumulators at Hkv, u16 key counts [B,Hkv,Sq,Skv]
     a = valid_args(topk_idx=0x100000, topk=2048, B=1, Sq=4096, Skv=8192, Hq=64, Hkv=1, Dqk=576, Dv=512)
-    assert ab.attn_bwd_workspace_size(a) == 2 * (64 * 4096 * 4) + 8192 * 576 * 4 + 8192 * 512 * 4
+    assert ab.attn_bwd_workspace_size(a) == 2 * (64 * 4096 * 4) + 8192 * 576 * 4 + 8192 * 512 * 4 + 4096 * 8192 * 2
+    # Skv is padded to a multiple of 32 in the count rows
+    a = valid_args(topk_idx=0x100000, topk=8, B=1, Sq=10, Skv=50, Hq=64, Hkv=1, Dqk=576, Dv=512)
+    assert ab.attn_bwd_workspace_size(a) == 2 * 2560 + 115200 + 102400 + 1280
 
 
 @pytest.mark.parametrize(
@@ -71,6 +74,7 @@ def test_workspace_size():
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, window=4), -1),  # no window with top-k
         (dict(topk_idx=0x100002, topk=8, Dqk=576, Dv=512), -1),  # misaligned index list
         (dict(topk_idx=0x100000, topk=0, Dqk=576, Dv=512), -1),
+        (dict(topk_idx=0x100000, topk=65536, Dqk=576, Dv=512), -2),  # key counts are 16-bit
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, workspace=0x100000, workspace_bytes=1 << 20), -3),
         (dict(workspace=0x100000, workspace_bytes=16), -3),
         (dict(workspace=0x100080, workspace_bytes=1 << 30), -1),  # workspace not 256-byte aligned
