@@ -90,17 +90,39 @@ __device__ __forceinline__ int swz(int row) {
   return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
 }
 
-// Asynchronous 16-byte copy global -> LDS: lane l of the wave writes lds_base + 16*l.
-// lds_base must be wave-uniform.  Completion is tracked by vmcnt (wait_vm0 below).
+// Asynchronous copy global -> LDS (global_load_lds): lane l of the wave writes lds_base + 16*l
+// (or 4*l).  lds_base must be wave-uniform; completion is tracked by vmcnt only (wait_vm0 below,
+// then a barrier before other waves read the data).
+// The instruction is issued from inline assembly on purpose: when the compiler sees an LDS DMA it
+// makes every later LDS read wait for all outstanding vector-memory operations unless it can
+// prove the two do not alias, which it cannot for a buffer picked at run time -- that turned
+// each step's prefetch of the next tile into a full stall before the step's first LDS read.
+// The kernels never read a buffer that has a copy in flight (they wait and synchronise first),
+// so no such wait is needed.  M0 carries the LDS base; one wait state separates its write from
+// the load.  Waits the compiler places for its own loads stay correct: loads complete in order,
+// so an extra load in flight can only make such a wait longer.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
 __device__ __forceinline__ void g2lds16(const void *g, void *lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                   (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base))), "v"(g)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void g2lds4(const void *g, void *lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                   (__attribute__((address_space(3))) void *)lds_base, 4, 0, 0);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base))), "v"(g)
+               : "memory", "m0");
 }
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait for every outstanding vector-memory operation (vmcnt = 0; expcnt and lgkmcnt left at their
+// no-wait maxima in the gfx9 encoding).  Issued through the builtin so that the compiler's own
+// wait placement knows the loads it issued itself are complete from here on.
+__device__ __forceinline__ void wait_vm0() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
 
 // Keeps the compiler's scheduler from moving instructions across this point: an operand read
 // issued ahead of the products that consume it stays ahead of them (the scheduler otherwise

@@ -101,17 +101,22 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   // Direct global->LDS tile loads: slot s of a tile is physical chunk s % CPR of row s / CPR and
   // holds logical chunk (s % CPR) ^ swz<D>(row).  Rows past the end are clamped to the last key
   // (their scores are masked).
-  auto issue = [&](int t, int buf) {
+  constexpr int NPART = 2 * C::WIW;
+  auto issue_part = [&](int t, int buf, int part) {
     const int k0 = (kb_lo + t) * BK;
-#pragma unroll
-    for (int u = 0; u < C::WIW; u++) {
-      const int slot0 = (w * C::WIW + u) * 64;
-      const int s = slot0 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz<D>(row);
-      const int kj = min(k0 + row, p.Skv - 1);
-      const int64_t o64 = ((int64_t)(b * p.Skv + kj) * p.Hkv + g) * D + 8 * ch;
-      g2lds16(p.k + o64, &k_s[buf][slot0 * 8]);
+    const int u = part >> 1;
+    const int slot0 = (w * C::WIW + u) * 64;
+    const int s = slot0 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz<D>(row);
+    const int kj = min(k0 + row, p.Skv - 1);
+    const int64_t o64 = ((int64_t)(b * p.Skv + kj) * p.Hkv + g) * D + 8 * ch;
+    if (part & 1)
       g2lds16(p.v + o64, &v_s[buf][slot0 * 8]);
-    }
+    else
+      g2lds16(p.k + o64, &k_s[buf][slot0 * 8]);
+  };
+  auto issue = [&](int t, int buf) {
+#pragma unroll
+    for (int part = 0; part < NPART; part++) issue_part(t, buf, part);
   };
 
   // Per-lane LDS offsets (elements): natural read of key row 32*kb + lo, logical chunk
@@ -134,9 +139,9 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   for (int t = 0; t < nsteps; t++) {
     const int buf = t & 1;
     const int k0 = (kb_lo + t) * BK;
-    if (t + 1 < nsteps) issue(t + 1, buf ^ 1);
     const bool active = qw0 < p.Sq && (!p.causal || k0 <= wlast + off) &&
                         (p.window <= 0 || k0 + BK - 1 > qw0 + off - p.window);
+    if (t + 1 < nsteps) issue(t + 1, buf ^ 1);
     if (active) {
       const bool full = (!p.causal || k0 + BK - 1 <= qw0 + off) && (p.window <= 0 || k0 > qw0 + 31 + off - p.window) &&
                         (k0 + BK <= p.Skv) && (qw0 + 32 <= p.Sq);

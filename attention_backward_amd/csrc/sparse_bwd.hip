@@ -64,6 +64,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
   __shared__ int idx_s[3][C::KC];  // key of each slot, -1 where the slot is masked
   __shared__ int row_s[3][C::KC];  // row gathered for each slot (a valid key of the chunk)
   __shared__ int any_s[3];         // whether the chunk has a valid slot
+  __shared__ int idx_raw[4][C::KC];  // list entries of chunks c+1..c+3, loaded three chunks ahead
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -116,6 +117,12 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
   const int32_t *idx_row = p.idx + (((int64_t)b * p.Sq + i) * p.Hkv + g) * p.topk;
   const int nchunks = (p.topk + C::KC - 1) / C::KC;
 
+  // Raw list entries of chunk c into idx_raw[c % 4] (wave 0, direct global->LDS loads, so that
+  // reading them never makes the compiler wait for the gathers in flight); entries past topk
+  // load the last entry and are dropped below.
+  auto load_idx = [&](int c) {
+    if (w == 0 && lane < C::KC) g2lds4(idx_row + min(c * C::KC + lane, p.topk - 1), &idx_raw[c & 3][0]);
+  };
   // Slots of chunk c (wave 0): a masked slot (padding, out of range, past the causal diagonal)
   // gathers the row of the chunk's first valid slot, so every gathered row is one this query
   // attends; its own P and dS are forced to zero.
@@ -124,7 +131,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
     int j = -1;
     if (lane < C::KC) {
       const int t = c * C::KC + lane;
-      j = t < p.topk ? idx_row[t] : -1;
+      j = t < p.topk ? idx_raw[c & 3][lane] : -1;
       if (j < 0 || j >= p.Skv || (p.causal && j > i + off)) j = -1;
     }
     const uint64_t m = __ballot(j >= 0);
@@ -167,6 +174,11 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
     return cat8(part[0], part[1]);
   };
 
+#pragma unroll
+  for (int c = 0; c < 3; c++)
+    if (c < nchunks) load_idx(c);
+  wait_vm0();
+  __syncthreads();
   if (w == 0) slots(0);
   __syncthreads();
   gather(0);
@@ -177,6 +189,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
   for (int c = 0; c < nchunks; c++) {
     const int buf = c & 1, sb = c % 3;
     if (c + 1 < nchunks) gather(c + 1);  // rows of chunk c+1 became visible at the last barrier
+    if (c + 3 < nchunks) load_idx(c + 3);  // consumed by slots(c + 3) in the next iteration
 
     // Phase A: partial S (waves 0-1) or dP (waves 2-3) over this wave's half of the head dim;
     // M = heads, N = slots.  B = K / V rows of the slots, natural reads through a ring; two
