@@ -144,8 +144,8 @@ int attn_bwd_ex(const attn_bwd_args *a) {
     if (e == hipSuccess)
       e = attn::launch_topk_count(a->topk_idx, cnt, a->B, a->Sq, a->Skv, a->Hkv, a->topk, (int)skv_pad(a), a->causal,
                                   st);
-    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
     if (e == hipSuccess) e = attn::launch_sparse_dq(p, bf16, st);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
     if (e == hipSuccess) e = attn::launch_sparse_dkdv(p, cnt, (int)skv_pad(a), dk_acc, dv_acc, bf16, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
     if (e == hipSuccess) e = attn::launch_land(dk_acc, p.dk, nk, a->scale, bf16, st);

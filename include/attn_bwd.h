@@ -85,9 +85,9 @@ typedef struct {
                                        caller, recorded on `stream` between the phases: dense =
                                        before the preprocess | after it | after the dK/dV kernel
                                        | after the dQ kernel; top-k = before the preprocess |
-                                       after it and the accumulator zero-fill | after the
-                                       gathered kernel | after the landing passes (per-phase
-                                       timing without changing the work)                     */
+                                       after it, the zero-fill, the key counts and the dQ
+                                       kernel | after the dK/dV kernel | after the landing
+                                       passes (per-phase timing without changing the work)   */
 } attn_bwd_args;
 
 /* Bytes of workspace the call needs for these sizes (0 if the arguments are invalid), as
