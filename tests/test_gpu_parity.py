@@ -65,7 +65,7 @@ SMALL = [
     small("swa_g8_d128_window37", B=1, Sq=333, Skv=333, Hq=8, Hkv=1, window=37, seed=106),
     small("swa_window1024_t2500", B=1, Sq=2500, Skv=2500, Hq=4, Hkv=2, Dqk=64, Dv=64, window=1024, seed=107),
     small("mha_causal_s1024_h4_bf16", Sq=1024, Skv=1024, Hq=4, Hkv=4, dtype="bf16", seed=108),
-] + [small(f"tiny_s{s}", Sq=s, Skv=s, seed=110 + s) for s in (1, 2, 63, 65, 127, 129)]
+] + [small(f"tiny_s{s}", Sq=s, Skv=s, seed=110 + s) for s in (1, 2, 63, 65, 127, 129, 200)]
 
 
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
