@@ -70,6 +70,20 @@ __device__ __forceinline__ s4v lds_tr4(const short *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v *)(p));
 }
 
+// The same reads at an LDS byte address: written as (lane base + compile-time offset), the
+// constant folds into the instruction's offset field instead of costing an add per read.
+__device__ __forceinline__ s4v lds_tr4_at(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v *)(size_t)a);
+}
+__device__ __forceinline__ s8v lds_rd16_at(uint32_t a) { return *(__attribute__((address_space(3))) s8v *)(size_t)a; }
+
+// A value the compiler must treat as computed here: keeps it from hoisting (address + constant)
+// sums out of a loop into one register each, which would cost an add per read inside the loop.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ s8v cat8(s4v a, s4v b) { return s8v{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 
 // LDS tiles are stored without row padding; the 16-byte chunk c of row R sits at chunk

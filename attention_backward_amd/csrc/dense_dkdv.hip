@@ -152,11 +152,25 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
   // acc += A^T B with B[k=query][n=d] read transposed from the row-major tile `src`.  The LDS
   // operands are read PF products ahead through a ring of registers, so that the read latency
   // hides behind the matrix core instead of stalling it before every product.
+  // Per-lane byte offsets of both reads within a tile; the step's tile base is added once per
+  // offset and the row-block offsets fold into the read instructions.
+  uint32_t tr_lane[C::ND][2], nat_lane[C::KK];
+#pragma unroll
+  for (int dn = 0; dn < C::ND; dn++)
+#pragma unroll
+    for (int half = 0; half < 2; half++) tr_lane[dn][half] = 2 * tr_off(0, dn, half);
+#pragma unroll
+  for (int kk = 0; kk < C::KK; kk++) nat_lane[kk] = 2 * nat_off(0, kk);
   auto phase2 = [&](const s8v *pa, const s8v *pl, const short *src) {
     constexpr int N = C::KS * C::ND, PF = ATTN_LDS_PREFETCH;
+    uint32_t ab[C::ND][2];
+#pragma unroll
+    for (int dn = 0; dn < C::ND; dn++)
+#pragma unroll
+      for (int half = 0; half < 2; half++) ab[dn][half] = opaque(lds_addr(src) + tr_lane[dn][half]);
     auto ld = [&](int n) {
       const int ks = n / C::ND, dn = n % C::ND;
-      return cat8(lds_tr4(&src[tr_off(ks, dn, 0)]), lds_tr4(&src[tr_off(ks, dn, 1)]));
+      return cat8(lds_tr4_at(ab[dn][0] + ks * 32 * D), lds_tr4_at(ab[dn][1] + ks * 32 * D));
     };
     s8v ring[PF + 1];
 #pragma unroll
@@ -175,7 +189,10 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
     constexpr int N = C::KK * C::MB, PF = ATTN_LDS_PREFETCH;
 #pragma unroll
     for (int mb = 0; mb < C::MB; mb++) s[mb] = f16v{};
-    auto ld = [&](int n) { return *(const s8v *)&src[nat_off(n % C::MB, n / C::MB)]; };
+    uint32_t ab[C::KK];
+#pragma unroll
+    for (int kk = 0; kk < C::KK; kk++) ab[kk] = opaque(lds_addr(src) + nat_lane[kk]);
+    auto ld = [&](int n) { return lds_rd16_at(ab[n / C::MB] + (n % C::MB) * 64 * D); };
     s8v ring[PF + 1];
 #pragma unroll
     for (int n = 0; n < PF; n++) ring[n] = ld(n);
