@@ -132,6 +132,17 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
     return (16 * kst + 8 * half + tr_row) * D + 8 * ch + 4 * (i16 & 1);
   };
 
+  // Per-lane byte offsets of both reads within a tile; each step adds its tile base once per
+  // offset (opaque, so the compiler cannot hoist one sum per read out of the loop) and the
+  // row-block offsets fold into the read instructions.
+  uint32_t nat_lane[C::KK], tr_lane[C::ND][2];
+#pragma unroll
+  for (int kk = 0; kk < C::KK; kk++) nat_lane[kk] = 2 * nat_off(0, kk);
+#pragma unroll
+  for (int dn = 0; dn < C::ND; dn++)
+#pragma unroll
+    for (int half = 0; half < 2; half++) tr_lane[dn][half] = 2 * tr_off(0, dn, half);
+
   if (nsteps > 0) issue(0, 0);
   wait_vm0();
   __syncthreads();
@@ -161,8 +172,14 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
           // K and V rows are read PF k-steps ahead through a ring of registers (the read
           // latency hides behind the matrix core); the fences keep that order.
           constexpr int N = C::KK * KBS, PF = ATTN_LDS_PREFETCH;
-          auto ldk = [&](int n) { return *(const s8v *)&ks[nat_off(sb * KBS + n % KBS, n / KBS)]; };
-          auto ldv = [&](int n) { return *(const s8v *)&vs[nat_off(sb * KBS + n % KBS, n / KBS)]; };
+          uint32_t abk[C::KK], abv[C::KK];
+#pragma unroll
+          for (int kk = 0; kk < C::KK; kk++) {
+            abk[kk] = opaque(lds_addr(ks) + nat_lane[kk]);
+            abv[kk] = opaque(lds_addr(vs) + nat_lane[kk]);
+          }
+          auto ldk = [&](int n) { return lds_rd16_at(abk[n / KBS] + (sb * KBS + n % KBS) * 64 * D); };
+          auto ldv = [&](int n) { return lds_rd16_at(abv[n / KBS] + (sb * KBS + n % KBS) * 64 * D); };
           s8v rk[PF + 1], rv[PF + 1];
 #pragma unroll
           for (int n = 0; n < PF; n++) {
@@ -207,9 +224,14 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
         mfma_prio_hi();
         {
           constexpr int N = KSTS * C::ND, PF = ATTN_LDS_PREFETCH;
+          uint32_t ab[C::ND][2];
+#pragma unroll
+          for (int dn = 0; dn < C::ND; dn++)
+#pragma unroll
+            for (int half = 0; half < 2; half++) ab[dn][half] = opaque(lds_addr(ks) + tr_lane[dn][half]);
           auto ld = [&](int n) {
             const int kg = sb * KSTS + n / C::ND, dn = n % C::ND;
-            return cat8(lds_tr4(&ks[tr_off(kg, dn, 0)]), lds_tr4(&ks[tr_off(kg, dn, 1)]));
+            return cat8(lds_tr4_at(ab[dn][0] + kg * 32 * D), lds_tr4_at(ab[dn][1] + kg * 32 * D));
           };
           s8v ring[PF + 1];
 #pragma unroll
