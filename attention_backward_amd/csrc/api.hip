@@ -104,7 +104,7 @@ int attn_bwd_ex(const attn_bwd_args *a) {
   p.v = (const short *)a->v;
   p.o = (const short *)a->o;
   p.dout = (const short *)a->dout;
-  p.delta = (float *)ws;
+  p.ndelta = (float *)ws;
   p.lse = (const float *)((char *)ws + row_stat_bytes(a));
   p.idx = a->topk_idx;
   p.dq = (short *)a->dq;
@@ -127,7 +127,7 @@ int attn_bwd_ex(const attn_bwd_args *a) {
   hipEvent_t *ev = (hipEvent_t *)a->events;
   hipError_t e = ev ? hipEventRecord(ev[0], st) : hipSuccess;
   if (e == hipSuccess)
-    e = attn::launch_delta(p.o, p.dout, p.delta, a->lse, (float *)p.lse, a->B, a->Sq, a->Hq, a->Dv, bf16, st);
+    e = attn::launch_delta(p.o, p.dout, p.ndelta, a->lse, (float *)p.lse, true, a->B, a->Sq, a->Hq, a->Dv, bf16, st);
   if (!a->topk_idx) {
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
     if (e == hipSuccess) e = attn::launch_dense_dkdv(p, bf16, st);
@@ -200,7 +200,7 @@ int attn_bwd_delta(const void *o, const void *dout, float *delta, int64_t B, int
   if (B < 1 || Sq < 1 || Hq < 1) return ATTN_E_INVAL;
   if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16) return ATTN_E_INVAL;
   if (Dv != 64 && Dv != 128 && Dv != 256 && Dv != 512) return ATTN_E_UNSUPPORTED;
-  hipError_t e = attn::launch_delta((const short *)o, (const short *)dout, delta, nullptr, nullptr, B, Sq, Hq, Dv,
+  hipError_t e = attn::launch_delta((const short *)o, (const short *)dout, delta, nullptr, nullptr, false, B, Sq, Hq, Dv,
                                     dtype == ATTN_DT_BF16, (hipStream_t)stream);
   if (e != hipSuccess) return set_hip_error(e, "delta launch");
   return ATTN_OK;

@@ -29,7 +29,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct Params {
   const short *q, *k, *v, *o, *dout;  // element bits of fp16/bf16
   const float *lse;                   // [B,Hq,Sq] base 2, -inf mapped to +inf (workspace copy)
-  float *delta;                       // [B,Hq,Sq] workspace
+  float *ndelta;                      // [B,Hq,Sq] workspace: minus rowsum(o * dout) (the negation
+                                      // lets dP accumulators start from it: dP - delta for free)
   const int32_t *idx;                 // [B,Sq,Hkv,topk] or null
   short *dq, *dk, *dv;
   int B, Sq, Skv, Hq, Hkv, G, topk, Dqk, Dv;

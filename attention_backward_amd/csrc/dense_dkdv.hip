@@ -114,7 +114,7 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
       if (w == 0)
         g2lds4(p.lse + li, &lse_s[buf][0]);
       else
-        g2lds4(p.delta + li, &dl_s[buf][0]);
+        g2lds4(p.ndelta + li, &dl_s[buf][0]);
     }
   };
 
@@ -185,10 +185,9 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
     }
   };
   // Phase 1 for M = the step's queries, N = this wave's keys, A rows from `src` (same ring).
+  // Accumulates into s as given (the caller sets its starting value).
   auto phase1 = [&](f16v *s, const short *src) {
     constexpr int N = C::KK * C::MB, PF = ATTN_LDS_PREFETCH;
-#pragma unroll
-    for (int mb = 0; mb < C::MB; mb++) s[mb] = f16v{};
     uint32_t ab[C::KK];
 #pragma unroll
     for (int kk = 0; kk < C::KK; kk++) ab[kk] = opaque(lds_addr(src) + nat_lane[kk]);
@@ -219,7 +218,7 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
       const int buf = t & 1;
       const int q0 = step_q0(t);
       if (t + 1 < nsteps) issue(t + 1, (t + 1) % 3, buf ^ 1);
-      f16v s[C::MB];
+      f16v s[C::MB] = {};
       mfma_prio_hi();
       phase1(s, q_s[t % 3]);
       mfma_prio_lo();
@@ -260,17 +259,26 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
       const int buf = t & 1;
       if (t + 1 < nsteps) issue(t + 1, (t + 1) % 3, buf ^ 1);
       if (t > 0) phase2(da, dl, q_s[(t + 2) % 3]);  // dK += dS^T Q of step t-1
+      // dP accumulators start from minus delta of their query rows (register 4 j + i of block mb
+      // is row 32 mb + 8 j + 4 hi + i), so the products leave dP - delta in them.
       f16v s[C::MB];
-      phase1(s, do_s[buf]);  // dP = dO V^T
-      __syncthreads();       // P of this step visible
 #pragma unroll
       for (int mb = 0; mb < C::MB; mb++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const f4v d4 = *(const f4v *)&dl_s[buf][32 * mb + 8 * j + 4 * hi];
+#pragma unroll
+          for (int i = 0; i < 4; i++) s[mb][4 * j + i] = d4[i];
+        }
+      phase1(s, do_s[buf]);  // dP - delta = dO V^T - delta
+      __syncthreads();       // P of this step visible
+#pragma unroll
+      for (int mb = 0; mb < C::MB; mb++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
           const f4v pq = p_s[kgrp][mb][j][lane];
 #pragma unroll
-          for (int i = 0; i < 4; i++) pack(da, dl, mb, 4 * j + i, pq[i] * (s[mb][4 * j + i] - d4[i]));
+          for (int i = 0; i < 4; i++) pack(da, dl, mb, 4 * j + i, pq[i] * s[mb][4 * j + i]);
         }
       wait_vm0();
       __syncthreads();  // next tile landed; P consumed

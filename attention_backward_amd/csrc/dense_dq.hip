@@ -80,7 +80,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   }
   const int64_t li = ((int64_t)b * p.Hq + h) * p.Sq + (qok ? qi : 0);
   const float lr = qok ? p.lse[li] : __builtin_inff();
-  const float dr = qok ? p.delta[li] : 0.f;
+  const float ndr = qok ? p.ndelta[li] : 0.f;  // minus delta
   const int klo = p.window > 0 ? qi + off - p.window + 1 : 0;
   const int khi = !qok ? klo - 1 : p.causal ? min(qi + off, p.Skv - 1) : p.Skv - 1;
 
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
                 const int kj = k0 + 32 * (sb * KBS + kb) + 8 * (r >> 2) + 4 * hi + (r & 3);
                 x = ((kj >= klo) & (kj <= khi)) ? x : 0.f;
               }
-              const float ds = x * (dp[kb][r] - dr);
+              const float ds = x * (dp[kb][r] + ndr);
               const short dh = TT::cvt(ds);
               da[2 * kb + (r >> 3)][r & 7] = dh;
               dl[2 * kb + (r >> 3)][r & 7] = TT::SPLIT ? TT::cvt(ds - TT::tof(dh)) : (short)0;

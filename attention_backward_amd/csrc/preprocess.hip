@@ -17,7 +17,8 @@ namespace attn {
 template <class TT, int DV>
 __global__ __launch_bounds__(256) void delta_kernel(const short *__restrict__ o, const short *__restrict__ dout,
                                                     float *__restrict__ delta, const float *__restrict__ lse_in,
-                                                    float *__restrict__ lse_out, int64_t rows, int Sq, int Hq) {
+                                                    float *__restrict__ lse_out, float sgn, int64_t rows, int Sq,
+                                                    int Hq) {
   constexpr int TPR = DV / 8;       // lanes per row (16 bytes each)
   constexpr int RPB = 256 / TPR;    // rows per block per iteration
   const int sub = threadIdx.x % TPR;
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const short *__restrict__ o,
       const int64_t i = (row / Hq) % Sq;
       const int64_t b = row / ((int64_t)Hq * Sq);
       const int64_t x = (b * Hq + h) * Sq + i;
-      delta[x] = acc;
+      delta[x] = sgn * acc;
       if (lse_in) lse_out[x] = lse_fix(lse_in[x]);
     }
   }
@@ -42,23 +43,23 @@ __global__ __launch_bounds__(256) void delta_kernel(const short *__restrict__ o,
 
 template <class TT, int DV>
 static hipError_t launch_delta_t(const short *o, const short *dout, float *delta, const float *lse_in, float *lse_out,
-                                 int64_t B, int64_t Sq, int64_t Hq, hipStream_t st) {
+                                 bool negate, int64_t B, int64_t Sq, int64_t Hq, hipStream_t st) {
   constexpr int RPB = 256 / (DV / 8);
   const int64_t rows = B * Sq * Hq;
   int64_t blocks = (rows + RPB - 1) / RPB;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) return hipSuccess;
   hipLaunchKernelGGL((delta_kernel<TT, DV>), dim3((unsigned)blocks), dim3(256), 0, st, o, dout, delta, lse_in, lse_out,
-                     rows, (int)Sq, (int)Hq);
+                     negate ? -1.f : 1.f, rows, (int)Sq, (int)Hq);
   return hipGetLastError();
 }
 
 hipError_t launch_delta(const short *o, const short *dout, float *delta, const float *lse_in, float *lse_out,
-                        int64_t B, int64_t Sq, int64_t Hq, int64_t Dv, bool bf16, hipStream_t st) {
+                        bool negate, int64_t B, int64_t Sq, int64_t Hq, int64_t Dv, bool bf16, hipStream_t st) {
 #define DISPATCH_DV(N)                                                                       \
   case N:                                                                                    \
-    return bf16 ? launch_delta_t<BF16, N>(o, dout, delta, lse_in, lse_out, B, Sq, Hq, st)    \
-                : launch_delta_t<F16, N>(o, dout, delta, lse_in, lse_out, B, Sq, Hq, st);
+    return bf16 ? launch_delta_t<BF16, N>(o, dout, delta, lse_in, lse_out, negate, B, Sq, Hq, st)    \
+                : launch_delta_t<F16, N>(o, dout, delta, lse_in, lse_out, negate, B, Sq, Hq, st);
   switch (Dv) {
     DISPATCH_DV(64)
     DISPATCH_DV(128)

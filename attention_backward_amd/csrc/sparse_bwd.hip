@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
     const int m = min(8 * (r >> 2) + 4 * hi + (r & 3), nh - 1);
     const int64_t li = ((int64_t)b * p.Hq + h0 + m) * p.Sq + i;
     lse_r[r] = p.lse[li];
-    dl_r[r] = p.delta[li];
+    dl_r[r] = p.ndelta[li];  // minus delta
   }
 
   // dQ accumulators: this wave owns the 32-wide d-blocks w, w+4, ... for the whole walk.
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
         const float dpv = part_s[2][r][lane] + part_s[3][r][lane];
         const bool ok = slot_ok && m < nh;
         const float pr = exp2f_hw(sv * p.c - lse_r[r]);
-        const float ds = ok ? pr * (dpv - dl_r[r]) : 0.f;
+        const float ds = ok ? pr * (dpv + dl_r[r]) : 0.f;
         const short dh = TT::cvt(ds);
         st_ds[0][m * C::KC + lo] = dh;
         if (TT::SPLIT) st_ds[1][m * C::KC + lo] = TT::cvt(ds - TT::tof(dh));

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
       if (w == 3)
         g2lds4(p.lse + li, &lse_s[buf][0]);
       else
-        g2lds4(p.delta + li, &dl_s[buf][0]);
+        g2lds4(p.ndelta + li, &dl_s[buf][0]);
     } else if (w == 1 && lane < C::BM / 2) {
       const int64_t e = (((int64_t)b * p.Hkv + g) * p.Sq + i) * skv_pad + j0 + 2 * lane;
       g2lds4(cnt + e, &cnt_s[buf][0]);
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
         const int key = 16 * kh + 4 * g16 + r;
         const float c = (float)cnt_s[buf][key];
         const float pr = (hok && c > 0.f) ? c * exp2f_hw(sv[r] * p.c - l) : 0.f;
-        const float ds = pr * (dpv[r] - dl);
+        const float ds = pr * (dpv[r] + dl);  // dl = minus delta
         const short ph = TT::cvt(pr), dh = TT::cvt(ds);
         st_p[0][key * C::HB + head] = ph;
         st_ds[0][key * C::HB + head] = dh;
