@@ -124,17 +124,21 @@ int attn_bwd_ex(const attn_bwd_args *a) {
   p.scale = a->scale;
   p.c = (float)((double)a->scale * 1.4426950408889634);
 
+  p.lse_in = a->lse;
+  p.lse_ws = (float *)p.lse;
+
   hipEvent_t *ev = (hipEvent_t *)a->events;
   hipError_t e = ev ? hipEventRecord(ev[0], st) : hipSuccess;
-  if (e == hipSuccess)
-    e = attn::launch_delta(p.o, p.dout, p.ndelta, a->lse, (float *)p.lse, true, a->B, a->Sq, a->Hq, a->Dv, bf16, st);
   if (!a->topk_idx) {
+    // The dQ kernel forms delta and the lse copy in its prologue, so it runs first.
+    if (e == hipSuccess) e = attn::launch_dense_dq(p, bf16, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
     if (e == hipSuccess) e = attn::launch_dense_dkdv(p, bf16, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
-    if (e == hipSuccess) e = attn::launch_dense_dq(p, bf16, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
   } else {
+    if (e == hipSuccess)
+      e = attn::launch_delta(p.o, p.dout, p.ndelta, a->lse, (float *)p.lse, true, a->B, a->Sq, a->Hq, a->Dv, bf16, st);
     float *dk_acc = (float *)((char *)ws + 2 * row_stat_bytes(a));
     float *dv_acc = (float *)((char *)dk_acc + dk_acc_bytes(a));
     uint16_t *cnt = (uint16_t *)((char *)dv_acc + dv_acc_bytes(a));

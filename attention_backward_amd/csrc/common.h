@@ -29,6 +29,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct Params {
   const short *q, *k, *v, *o, *dout;  // element bits of fp16/bf16
   const float *lse;                   // [B,Hq,Sq] base 2, -inf mapped to +inf (workspace copy)
+  const float *lse_in;                // the caller's lse (dense dQ kernel: input of its prologue)
+  float *lse_ws;                      // the workspace copy the dense dQ kernel writes
   float *ndelta;                      // [B,Hq,Sq] workspace: minus rowsum(o * dout) (the negation
                                       // lets dP accumulators start from it: dP - delta for free)
   const int32_t *idx;                 // [B,Sq,Hkv,topk] or null

@@ -78,9 +78,28 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
       dof[kk] = qok ? *(const s8v *)(p.dout + o64 + 16 * kk) : s8v{};
     }
   }
+  // The preprocess runs here, in the prologue: delta = rowsum(O * dO) of the lane's query row
+  // (split over the two lane halves like the dO operand; one cross-half add completes it) and lse
+  // with -inf mapped to +inf.  Both also go to the workspace (delta negated) for the dK/dV
+  // kernel, which runs after this one.
   const int64_t li = ((int64_t)b * p.Hq + h) * p.Sq + (qok ? qi : 0);
-  const float lr = qok ? p.lse[li] : __builtin_inff();
-  const float ndr = qok ? p.ndelta[li] : 0.f;  // minus delta
+  float dsum = 0.f;
+  if (qok) {
+    const short *orow = p.o + ((int64_t)(b * p.Sq + qi) * p.Hq + h) * D + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; kk++) {
+      const s8v ov = *(const s8v *)(orow + 16 * kk);
+#pragma unroll
+      for (int e = 0; e < 8; e++) dsum += TT::tof(ov[e]) * TT::tof(dof[kk][e]);
+    }
+  }
+  dsum += __shfl_xor(dsum, 32);
+  const float lr = qok ? lse_fix(p.lse_in[li]) : __builtin_inff();
+  const float ndr = -dsum;  // minus delta
+  if (qok && hi == 0) {
+    p.ndelta[li] = ndr;
+    p.lse_ws[li] = lr;
+  }
   const int klo = p.window > 0 ? qi + off - p.window + 1 : 0;
   const int khi = !qok ? klo - 1 : p.causal ? min(qi + off, p.Skv - 1) : p.Skv - 1;
 

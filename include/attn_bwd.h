@@ -83,16 +83,17 @@ typedef struct {
   void *stream;                     /* hipStream_t                                             */
   void *events;                     /* optional, NULL or an array of 4 hipEvent_t created by the
                                        caller, recorded on `stream` between the phases: dense =
-                                       before the preprocess | after it | after the dK/dV kernel
-                                       | after the dQ kernel; top-k = before the preprocess |
-                                       after it, the zero-fill, the key counts and the dQ
-                                       kernel | after the dK/dV kernel | after the landing
-                                       passes (per-phase timing without changing the work)   */
+                                       before the dQ kernel (which also forms delta and the lse
+                                       copy) | after it | after the dK/dV kernel | again after
+                                       the dK/dV kernel; top-k = before the preprocess | after
+                                       it, the zero-fill, the key counts and the dQ kernel |
+                                       after the dK/dV kernel | after the landing passes
+                                       (per-phase timing without changing the work)          */
 } attn_bwd_args;
 
 /* Bytes of workspace the call needs for these sizes (0 if the arguments are invalid), as
  * 256-byte aligned parts:
- *   delta and a sanitised copy of lse, [B,Hq,Sq] f32 each;
+ *   delta (stored negated) and a sanitised copy of lse, [B,Hq,Sq] f32 each;
  *   top-k only: f32 accumulators dK_acc [B,Skv,Hkv,Dqk] and dV_acc [B,Skv,Hkv,Dv].
  * Never an Hq-shaped dK/dV buffer.  Top-k results: dq is written once per element; dk and dv
  * are sums of f32 atomic additions, so their last bits may differ between identical calls. */
