@@ -46,6 +46,8 @@ int validate_sizes(const attn_bwd_args *a) {
   if (a->topk_idx) {
     if (a->topk > 65535) return ATTN_E_UNSUPPORTED;  // 16-bit key counts
     if (!(a->Dqk == 576 && a->Dv == 512)) return ATTN_E_UNSUPPORTED;
+    // The gathers address one (batch, KV head)'s K or V rows with 32-bit byte offsets.
+    if (a->Skv * a->Hkv * a->Dqk * 2 >= ((int64_t)1 << 32)) return ATTN_E_UNSUPPORTED;
   } else if (!((a->Dqk == 64 && a->Dv == 64) || (a->Dqk == 128 && a->Dv == 128))) {
     return ATTN_E_UNSUPPORTED;
   }

@@ -133,6 +133,33 @@ __device__ __forceinline__ void g2lds4(const void *g, void *lds_base) {
                : "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base))), "v"(g)
                : "memory", "m0");
 }
+// The same copies through a buffer resource (buffer_load ... lds): measured on MI355X, a wave
+// issuing global_load_lds_dwordx4 moves about 5 B/clk (about 20 B/clk for four waves of a CU),
+// while buffer_load_dwordx4 ... lds, like plain vector loads, reaches the CU's ~60 B/clk with four
+// waves.  The resource covers `bytes` bytes from a wave-uniform `base` (loads beyond read 0);
+// each lane passes its byte offset from base.  Waits as for g2lds16 (vmcnt).
+typedef int i4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i4v buf_rsrc(const void *base, uint64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i4v r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0: raw bytes
+  r[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(bytes > 0xffffffffull ? 0xffffffffull : bytes));
+  r[3] = 0x00020000;  // 32-bit data format, no swizzle
+  return r;
+}
+__device__ __forceinline__ void b2lds16(i4v r, uint32_t voff, void *lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base))), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void b2lds4(i4v r, uint32_t voff, void *lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base))), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
 // Wait for every outstanding vector-memory operation (vmcnt = 0; expcnt and lgkmcnt left at their
 // no-wait maxima in the gfx9 encoding).  Issued through the builtin so that the compiler's own
 // wait placement knows the loads it issued itself are complete from here on.

@@ -120,8 +120,9 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
   // Raw list entries of chunk c into idx_raw[c % 4] (wave 0, direct global->LDS loads, so that
   // reading them never makes the compiler wait for the gathers in flight); entries past topk
   // load the last entry and are dropped below.
+  const i4v ridx = buf_rsrc(idx_row, (uint64_t)p.topk * 4);
   auto load_idx = [&](int c) {
-    if (w == 0 && lane < C::KC) g2lds4(idx_row + min(c * C::KC + lane, p.topk - 1), &idx_raw[c & 3][0]);
+    if (w == 0 && lane < C::KC) b2lds4(ridx, (uint32_t)min(c * C::KC + lane, p.topk - 1) * 4, &idx_raw[c & 3][0]);
   };
   // Slots of chunk c (wave 0): a masked slot (padding, out of range, past the causal diagonal)
   // gathers the row of the chunk's first valid slot, so every gathered row is one this query
@@ -142,21 +143,26 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
     }
     if (lane == 0) any_s[buf] = m != 0;
   };
+  // Gathers through buffer resources over this (batch, KV head)'s K and V rows; a row's byte
+  // offset is row * Hkv * D * 2 (the host checks it fits 32 bits).
+  const int64_t kv0 = (int64_t)b * p.Skv * p.Hkv + g, nkv = (int64_t)p.B * p.Skv * p.Hkv;
+  const i4v rk = buf_rsrc(p.k + kv0 * DQK, (uint64_t)(nkv - kv0) * DQK * 2);
+  const i4v rv = buf_rsrc(p.v + kv0 * DV, (uint64_t)(nkv - kv0) * DV * 2);
   auto gather = [&](int c) {
     const int buf = c & 1, sb = c % 3;
 #pragma unroll
     for (int u = 0; u < C::KC * C::CQ / 256; u++) {
       const int s = 256 * u + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sp_sw<DQK>(r);
-      g2lds16(p.k + (((int64_t)b * p.Skv + row_s[sb][r]) * p.Hkv + g) * DQK + 8 * ch, &k_s[buf][(s - lane) * 8]);
+      b2lds16(rk, ((uint32_t)row_s[sb][r] * p.Hkv * DQK + 8 * ch) * 2, &k_s[buf][(s - lane) * 8]);
     }
     if (C::KC * C::CQ % 256 != 0 && tid < C::KC * C::CQ % 256) {
       const int s = C::KC * C::CQ / 256 * 256 + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sp_sw<DQK>(r);
-      g2lds16(p.k + (((int64_t)b * p.Skv + row_s[sb][r]) * p.Hkv + g) * DQK + 8 * ch, &k_s[buf][(s - lane) * 8]);
+      b2lds16(rk, ((uint32_t)row_s[sb][r] * p.Hkv * DQK + 8 * ch) * 2, &k_s[buf][(s - lane) * 8]);
     }
 #pragma unroll
     for (int u = 0; u < C::KC * C::CV / 256; u++) {
       const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sp_sw<DV>(r);
-      g2lds16(p.v + (((int64_t)b * p.Skv + row_s[sb][r]) * p.Hkv + g) * DV + 8 * ch, &v_s[buf][(s - lane) * 8]);
+      b2lds16(rv, ((uint32_t)row_s[sb][r] * p.Hkv * DV + 8 * ch) * 2, &v_s[buf][(s - lane) * 8]);
     }
   };
   // B[k][n] = tile[row = 16*ks + 8*hi + e][col = 32*nb + lo] by transposed reads of a row-major

@@ -156,30 +156,34 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
     const int i = i_beg + t / nhb, hb0 = (t % nhb) * C::HB;
     const int nh = min(C::HB, p.G - hb0);
     const int64_t qrow = ((int64_t)b * p.Sq + i) * p.Hq + g * p.G + hb0;
+    const int64_t nrows = (int64_t)p.B * p.Sq * p.Hq;
+    const i4v rq = buf_rsrc(p.q + qrow * DQK, (uint64_t)(nrows - qrow) * DQK * 2);
+    const i4v rd = buf_rsrc(p.dout + qrow * DV, (uint64_t)(nrows - qrow) * DV * 2);
 #pragma unroll
     for (int u = 0; u < C::HB * C::CQ / 256; u++) {
       const int s = 256 * u + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sk_sw<DQK>(r);
-      g2lds16(p.q + (qrow + min(r, nh - 1)) * DQK + 8 * ch, &q_s[buf][(s - lane) * 8]);
+      b2lds16(rq, (uint32_t)(min(r, nh - 1) * DQK + 8 * ch) * 2, &q_s[buf][(s - lane) * 8]);
     }
     if (C::HB * C::CQ % 256 != 0 && tid < C::HB * C::CQ % 256) {
       const int s = C::HB * C::CQ / 256 * 256 + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sk_sw<DQK>(r);
-      g2lds16(p.q + (qrow + min(r, nh - 1)) * DQK + 8 * ch, &q_s[buf][(s - lane) * 8]);
+      b2lds16(rq, (uint32_t)(min(r, nh - 1) * DQK + 8 * ch) * 2, &q_s[buf][(s - lane) * 8]);
     }
 #pragma unroll
     for (int u = 0; u < C::HB * C::CV / 256; u++) {
       const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sk_sw<DV>(r);
-      g2lds16(p.dout + (qrow + min(r, nh - 1)) * DV + 8 * ch, &do_s[buf][(s - lane) * 8]);
+      b2lds16(rd, (uint32_t)(min(r, nh - 1) * DV + 8 * ch) * 2, &do_s[buf][(s - lane) * 8]);
     }
     // One wave per small row (the LDS base of a direct load is per wave): lane l writes word l.
-    if (w >= 2 && lane < C::HB) {
-      const int64_t li = ((int64_t)b * p.Hq + g * p.G + hb0 + min(lane, nh - 1)) * p.Sq + i;
-      if (w == 3)
-        g2lds4(p.lse + li, &lse_s[buf][0]);
-      else
-        g2lds4(p.ndelta + li, &dl_s[buf][0]);
-    } else if (w == 1 && lane < C::BM / 2) {
-      const int64_t e = (((int64_t)b * p.Hkv + g) * p.Sq + i) * skv_pad + j0 + 2 * lane;
-      g2lds4(cnt + e, &cnt_s[buf][0]);
+    if (w >= 2) {
+      const int64_t l0 = ((int64_t)b * p.Hq + g * p.G + hb0) * p.Sq + i;
+      const int64_t nl = (int64_t)p.B * p.Hq * p.Sq;
+      const i4v rl = buf_rsrc((w == 3 ? (const float *)p.lse : (const float *)p.ndelta) + l0, (uint64_t)(nl - l0) * 4);
+      if (lane < C::HB) b2lds4(rl, (uint32_t)(min(lane, nh - 1) * p.Sq) * 4, w == 3 ? &lse_s[buf][0] : &dl_s[buf][0]);
+    } else if (w == 1) {
+      const int64_t e0 = (((int64_t)b * p.Hkv + g) * p.Sq + i) * skv_pad + j0;
+      const int64_t ne = (int64_t)p.B * p.Hkv * p.Sq * skv_pad;
+      const i4v rc = buf_rsrc(cnt + e0, (uint64_t)(ne - e0) * 2);
+      if (lane < C::BM / 2) b2lds4(rc, (uint32_t)(4 * lane), &cnt_s[buf][0]);
     }
   };
 

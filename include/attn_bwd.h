@@ -65,7 +65,8 @@ typedef enum {
 } attn_status;
 
 /* Full argument set.  Sizes are int64; Sq != Skv and Dqk != Dv are allowed where a kernel
- * exists: dense (Dqk, Dv) in {(64,64), (128,128)}; top-k (Dqk, Dv) = (576, 512). */
+ * exists: dense (Dqk, Dv) in {(64,64), (128,128)}; top-k (Dqk, Dv) = (576, 512) with
+ * Skv * Hkv * Dqk * 2 < 2^32 (ATTN_E_UNSUPPORTED otherwise). */
 typedef struct {
   const void *q, *k, *v, *o, *dout; /* 16-byte aligned device pointers, element type = dtype   */
   const float *lse;                 /* [B, Hq, Sq] float32, base-2 log-sum-exp of the forward   */

@@ -75,6 +75,8 @@ def test_workspace_size():
         (dict(topk_idx=0x100002, topk=8, Dqk=576, Dv=512), -1),  # misaligned index list
         (dict(topk_idx=0x100000, topk=0, Dqk=576, Dv=512), -1),
         (dict(topk_idx=0x100000, topk=65536, Dqk=576, Dv=512), -2),  # key counts are 16-bit
+        # gathers use 32-bit byte offsets within one (batch, KV head)'s K rows
+        (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, Skv=1 << 22, Hkv=1, Hq=64), -2),
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, workspace=0x100000, workspace_bytes=1 << 20), -3),
         (dict(workspace=0x100000, workspace_bytes=16), -3),
         (dict(workspace=0x100080, workspace_bytes=1 << 30), -1),  # workspace not 256-byte aligned
