@@ -70,10 +70,22 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5, lo = lane & 31;
   const int i16 = lane & 15, g16 = lane >> 4;
+  // Workgroups of the same (query row, KV head) gather the same K/V rows: the nhb head blocks of
+  // one query are placed 8 apart in the dispatch order, which the hardware hands to the same XCD
+  // at about the same time, so most second gathers of a row hit that XCD's L2.
   const int nhb = (p.G + C::HB - 1) / C::HB;
   int x = blockIdx.x;
-  const int hb = x % nhb;
-  x /= nhb;
+  int hb;
+  {
+    const int grp = 8 * nhb, gi = x / grp, r = x % grp;
+    if ((gi + 1) * 8 <= p.B * p.Sq * p.Hkv) {  // a full group of 8 queries
+      hb = r / 8;
+      x = gi * 8 + r % 8;
+    } else {  // the ragged last group keeps the plain order
+      hb = r % nhb;
+      x = gi * 8 + r / nhb;
+    }
+  }
   const int g = x % p.Hkv;
   x /= p.Hkv;
   const int i = x % p.Sq;
