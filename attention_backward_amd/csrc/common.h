@@ -86,6 +86,14 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+// sbase + voff as one add the compiler cannot see into: it keeps the compiler from hoisting
+// (address + constant) sums out of a loop into one register each, which would cost an add per
+// read inside the loop; with this the constants fold into the reads' offset fields.
+__device__ __forceinline__ uint32_t lds_base_add(uint32_t sbase, uint32_t voff) {
+  uint32_t r;
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(__builtin_amdgcn_readfirstlane(sbase)), "v"(voff));
+  return r;
+}
 
 __device__ __forceinline__ s8v cat8(s4v a, s4v b) { return s8v{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 

@@ -50,8 +50,8 @@ struct DqCfg {
 template <class TT, int D, int BK, int SB>
 __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   using C = DqCfg<D, BK, SB>;
-  __shared__ __attribute__((aligned(16))) short k_s[2][BK * D];
-  __shared__ __attribute__((aligned(16))) short v_s[2][BK * D];
+  // [buffer][K, V][tile]: one array, so that a V read is the matching K read plus a constant.
+  __shared__ __attribute__((aligned(16))) short kv_s[2][2][BK * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -100,6 +100,10 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
     p.ndelta[li] = ndr;
     p.lse_ws[li] = lr;
   }
+  // Starting value of every dP accumulator: minus delta of the lane's query column.
+  f16v ndr16;
+#pragma unroll
+  for (int r = 0; r < 16; r++) ndr16[r] = ndr;
   const int klo = p.window > 0 ? qi + off - p.window + 1 : 0;
   const int khi = !qok ? klo - 1 : p.causal ? min(qi + off, p.Skv - 1) : p.Skv - 1;
 
@@ -129,9 +133,9 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
     const int kj = min(k0 + row, p.Skv - 1);
     const int64_t o64 = ((int64_t)(b * p.Skv + kj) * p.Hkv + g) * D + 8 * ch;
     if (part & 1)
-      g2lds16(p.v + o64, &v_s[buf][slot0 * 8]);
+      g2lds16(p.v + o64, &kv_s[buf][1][slot0 * 8]);
     else
-      g2lds16(p.k + o64, &k_s[buf][slot0 * 8]);
+      g2lds16(p.k + o64, &kv_s[buf][0][slot0 * 8]);
   };
   auto issue = [&](int t, int buf) {
 #pragma unroll
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   };
 
   // Per-lane byte offsets of both reads within a tile; each step adds its tile base once per
-  // offset (opaque, so the compiler cannot hoist one sum per read out of the loop) and the
+  // offset (one add the compiler cannot hoist as a sum per read out of the loop) and the
   // row-block offsets fold into the read instructions.
   uint32_t nat_lane[C::KK], tr_lane[C::ND][2];
 #pragma unroll
@@ -175,8 +179,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
     if (active) {
       const bool full = (!p.causal || k0 + BK - 1 <= qw0 + off) && (p.window <= 0 || k0 > qw0 + 31 + off - p.window) &&
                         (k0 + BK <= p.Skv) && (qw0 + 32 <= p.Sq);
-      const short *ks = k_s[buf];
-      const short *vs = v_s[buf];
+      const short *ks = kv_s[buf][0];
       // The tile is taken as SB sub-blocks of KS = BK / SB keys, one after the other: each forms
       // S^T = K Q^T and dP^T = V dO^T (M = keys in 32-row blocks, N = this wave's 32 queries), the
       // softmax gradient, and dQ += dS K.  Fewer keys at a time hold fewer accumulators live.
@@ -185,20 +188,20 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
         constexpr int KBS = C::KB / C::SB, KSTS = C::KST / C::SB;
         f16v s[KBS], dp[KBS];
 #pragma unroll
-        for (int kb = 0; kb < KBS; kb++) s[kb] = dp[kb] = f16v{};
+        for (int kb = 0; kb < KBS; kb++) {
+          s[kb] = f16v{};
+          dp[kb] = ndr16;  // the products leave dP - delta
+        }
         mfma_prio_hi();
         {
           // K and V rows are read PF k-steps ahead through a ring of registers (the read
           // latency hides behind the matrix core); the fences keep that order.
           constexpr int N = C::KK * KBS, PF = ATTN_LDS_PREFETCH;
-          uint32_t abk[C::KK], abv[C::KK];
+          uint32_t abk[C::KK];
 #pragma unroll
-          for (int kk = 0; kk < C::KK; kk++) {
-            abk[kk] = opaque(lds_addr(ks) + nat_lane[kk]);
-            abv[kk] = opaque(lds_addr(vs) + nat_lane[kk]);
-          }
+          for (int kk = 0; kk < C::KK; kk++) abk[kk] = lds_base_add(lds_addr(ks), nat_lane[kk]);
           auto ldk = [&](int n) { return lds_rd16_at(abk[n / KBS] + (sb * KBS + n % KBS) * 64 * D); };
-          auto ldv = [&](int n) { return lds_rd16_at(abv[n / KBS] + (sb * KBS + n % KBS) * 64 * D); };
+          auto ldv = [&](int n) { return lds_rd16_at(abk[n / KBS] + (sb * KBS + n % KBS) * 64 * D + BK * D * 2); };
           s8v rk[PF + 1], rv[PF + 1];
 #pragma unroll
           for (int n = 0; n < PF; n++) {
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
                 const int kj = k0 + 32 * (sb * KBS + kb) + 8 * (r >> 2) + 4 * hi + (r & 3);
                 x = ((kj >= klo) & (kj <= khi)) ? x : 0.f;
               }
-              const float ds = x * (dp[kb][r] + ndr);
+              const float ds = x * dp[kb][r];
               const short dh = TT::cvt(ds);
               da[2 * kb + (r >> 3)][r & 7] = dh;
               dl[2 * kb + (r >> 3)][r & 7] = TT::SPLIT ? TT::cvt(ds - TT::tof(dh)) : (short)0;
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
 #pragma unroll
           for (int dn = 0; dn < C::ND; dn++)
 #pragma unroll
-            for (int half = 0; half < 2; half++) ab[dn][half] = opaque(lds_addr(ks) + tr_lane[dn][half]);
+            for (int half = 0; half < 2; half++) ab[dn][half] = lds_base_add(lds_addr(ks), tr_lane[dn][half]);
           auto ld = [&](int n) {
             const int kg = sb * KSTS + n / C::ND, dn = n % C::ND;
             return cat8(lds_tr4_at(ab[dn][0] + kg * 32 * D), lds_tr4_at(ab[dn][1] + kg * 32 * D));
