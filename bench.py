@@ -344,9 +344,9 @@ def main():
                      "algorithmic_flops_per_launch": main_flops},
         "kernels_us_median": {kname: round(v_, 2) for kname, v_ in med.items()},
         "kernels": kernels,
-        "cold_call_us": {"median": round(statistics.median(cold), 2), "min": round(min(cold), 2),
-                         "max": round(max(cold), 2), "n": len(cold),
-                         "tflops_at_median": round(flops / (statistics.median(cold) * 1e-6) / 1e12, 1)},
+        "cold_call_us": None if not cold else {
+            "median": round(statistics.median(cold), 2), "min": round(min(cold), 2), "max": round(max(cold), 2),
+            "n": len(cold), "tflops_at_median": round(flops / (statistics.median(cold) * 1e-6) / 1e12, 1)},
     }
     if not args.no_cpu_baseline:
         inp_cpu = {n: inp[n] for n in ("q", "k", "v", "dout", "idx")}
