@@ -212,8 +212,9 @@ def main():
                          "kernel against which profiler byte counters are scaled)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this backward needs no inter-GPU communication; "
-              "run it with --gpus 1 (see the sharding note in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the backward runs on one GPU and this library has no "
+              "multi-GPU path (it would shard by (batch, head) or by query rows); run it with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import attention_backward_amd as ab

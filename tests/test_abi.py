@@ -90,7 +90,7 @@ def test_validation_statuses(kw, status):
     assert ab.attn_bwd_strerror(rc)
 
 
-def test_north_star_entry_point_validates():
+def test_plain_entry_point_validates():
     lib = ab.load()
     rc = lib.attn_bwd(None, None, None, None, None, None, None, None, None, 1, 128, 2, 2, 128, 0.1, 1, 0, None, 0, 0,
                       None, 0, None)
