@@ -180,6 +180,11 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
       const bool full = (!p.causal || k0 + BK - 1 <= qw0 + off) && (p.window <= 0 || k0 > qw0 + 31 + off - p.window) &&
                         (k0 + BK <= p.Skv) && (qw0 + 32 <= p.Sq);
       const short *ks = kv_s[buf][0];
+      // Read bases of this step's tile for the natural K/V reads; the sub-block and row-block
+      // offsets fold into the reads' offset fields.
+      uint32_t abk[C::KK];
+#pragma unroll
+      for (int kk = 0; kk < C::KK; kk++) abk[kk] = lds_base_add(lds_addr(ks), nat_lane[kk]);
       // The tile is taken as SB sub-blocks of KS = BK / SB keys, one after the other: each forms
       // S^T = K Q^T and dP^T = V dO^T (M = keys in 32-row blocks, N = this wave's 32 queries), the
       // softmax gradient, and dQ += dS K.  Fewer keys at a time hold fewer accumulators live.
@@ -197,9 +202,6 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
           // K and V rows are read PF k-steps ahead through a ring of registers (the read
           // latency hides behind the matrix core); the fences keep that order.
           constexpr int N = C::KK * KBS, PF = ATTN_LDS_PREFETCH;
-          uint32_t abk[C::KK];
-#pragma unroll
-          for (int kk = 0; kk < C::KK; kk++) abk[kk] = lds_base_add(lds_addr(ks), nat_lane[kk]);
           auto ldk = [&](int n) { return lds_rd16_at(abk[n / KBS] + (sb * KBS + n % KBS) * 64 * D); };
           auto ldv = [&](int n) { return lds_rd16_at(abk[n / KBS] + (sb * KBS + n % KBS) * 64 * D + BK * D * 2); };
           s8v rk[PF + 1], rv[PF + 1];
