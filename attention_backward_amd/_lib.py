@@ -137,7 +137,7 @@ def attn_bwd_ex(args: attn_bwd_args) -> None:
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, S, Hq, Hkv, D, scale, causal, window, topk_idx=None, topk=0,
              dtype=None, workspace=None, workspace_bytes=0, stream=None) -> None:
-    """The spec ordered entry point (Sq = Skv = S, Dqk = Dv = D), tensors or raw pointers."""
+    """The plain-argument entry point (Sq = Skv = S, Dqk = Dv = D), tensors or raw pointers."""
     ptr = lambda t: t.data_ptr() if isinstance(t, torch.Tensor) else t  # noqa: E731
     if dtype is None:
         dtype = _DT[q.dtype]

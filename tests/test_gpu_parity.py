@@ -80,7 +80,7 @@ def test_deterministic_and_both_entry_points():
     b = run(inp, w)
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16)), "outputs differ between two identical calls"
-    # the spec ordered entry point gives the same bits
+    # the plain-argument entry point gives the same bits
     g = to_gpu(inp)
     dq, dk, dv = poisoned_like(g["q"]), poisoned_like(g["k"]), poisoned_like(g["v"])
     ab.attn_bwd(g["q"], g["k"], g["v"], g["o"], g["dout"], g["lse"], dq, dk, dv, w.B, w.Sq, w.Hq, w.Hkv, w.Dqk,
