@@ -35,6 +35,7 @@ class attn_bwd_args(ctypes.Structure):  # noqa: N801  (mirrors the C struct name
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("events", ctypes.c_void_p),
+        ("kv_shared", ctypes.c_int32),
     ]
 
 
@@ -100,20 +101,26 @@ def _stream(stream):
 
 
 def make_args(q, k, v, o, dout, lse, dq, dk, dv, *, scale, causal=True, window=0, topk_idx=None,
-              workspace=None, stream=None) -> attn_bwd_args:
-    """Fill an attn_bwd_args from torch tensors (shapes taken from q [B,Sq,Hq,Dqk], k, v)."""
+              workspace=None, stream=None, kv_shared=False) -> attn_bwd_args:
+    """Fill an attn_bwd_args from torch tensors (shapes taken from q [B,Sq,Hq,Dqk], k and dout).
+
+    kv_shared: the shared-latent form of the top-k path; v and dv are None, V is the first Dv
+    columns of k and dk receives dK + [dV, 0]."""
     if q.dtype not in _DT:
         raise TypeError(f"unsupported dtype {q.dtype}")
+    if kv_shared and (v is not None or dv is not None):
+        raise ValueError("kv_shared: pass v=None and dv=None (V is read from k, dV is added into dk)")
     dt = q.dtype
     B, Sq, Hq, Dqk = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
-    Dv = v.shape[3]
+    Dv = dout.shape[3]
     a = attn_bwd_args()
     a.q, a.k, a.v = _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt)
     a.o, a.dout = _dev(o, "o", dt), _dev(dout, "dout", dt)
     a.lse = _dev(lse, "lse", torch.float32)
     a.topk_idx = _dev(topk_idx, "topk_idx", torch.int32)
     a.dq, a.dk, a.dv = _dev(dq, "dq", dt), _dev(dk, "dk", dt), _dev(dv, "dv", dt)
+    a.kv_shared = int(bool(kv_shared))
     a.B, a.Sq, a.Skv, a.Hq, a.Hkv, a.Dqk, a.Dv = B, Sq, Skv, Hq, Hkv, Dqk, Dv
     a.topk = 0 if topk_idx is None else topk_idx.shape[-1]
     a.scale = float(scale)

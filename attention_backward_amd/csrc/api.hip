@@ -40,6 +40,8 @@ int validate_sizes(const attn_bwd_args *a) {
   if (!a->topk_idx && a->topk != 0) return ATTN_E_INVAL;
   if (!(a->scale > 0.f) || !isfinite(a->scale)) return ATTN_E_INVAL;
   if (a->dtype != ATTN_DT_F16 && a->dtype != ATTN_DT_BF16) return ATTN_E_INVAL;
+  if (a->kv_shared != 0 && a->kv_shared != 1) return ATTN_E_INVAL;
+  if (a->kv_shared && !a->topk_idx) return ATTN_E_UNSUPPORTED;  // the dense kernels have no shared form
   // 32-bit row indices inside the kernels: every row count must fit comfortably.
   const int64_t lim = (int64_t)1 << 31;
   if (a->B * a->Sq * a->Hq >= lim || a->B * a->Skv * a->Hkv >= lim) return ATTN_E_UNSUPPORTED;
@@ -80,7 +82,10 @@ size_t attn_bwd_workspace_size(const attn_bwd_args *a) {
 int attn_bwd_ex(const attn_bwd_args *a) {
   int rc = validate_sizes(a);
   if (rc != ATTN_OK) return rc;
-  const void *ptrs[] = {a->q, a->k, a->v, a->o, a->dout, a->lse, a->dq, a->dk, a->dv};
+  // Shared-latent form: V is read from k and dV is added into dk, so v and dv must be NULL.
+  const bool shared = a->kv_shared != 0;
+  if (shared && (a->v || a->dv)) return ATTN_E_INVAL;
+  const void *ptrs[] = {a->q, a->k, shared ? a->k : a->v, a->o, a->dout, a->lse, a->dq, a->dk, shared ? a->dk : a->dv};
   for (const void *p : ptrs)
     if (!p || !aligned16(p)) return ATTN_E_INVAL;
   if (a->topk_idx && ((uintptr_t)a->topk_idx & 3) != 0) return ATTN_E_INVAL;
@@ -103,7 +108,8 @@ int attn_bwd_ex(const attn_bwd_args *a) {
   attn::Params p;
   p.q = (const short *)a->q;
   p.k = (const short *)a->k;
-  p.v = (const short *)a->v;
+  p.v = (const short *)(shared ? a->k : a->v);
+  p.v_ld = (int)(shared ? a->Dqk : a->Dv);
   p.o = (const short *)a->o;
   p.dout = (const short *)a->dout;
   p.ndelta = (float *)ws;
@@ -111,7 +117,7 @@ int attn_bwd_ex(const attn_bwd_args *a) {
   p.idx = a->topk_idx;
   p.dq = (short *)a->dq;
   p.dk = (short *)a->dk;
-  p.dv = (short *)a->dv;
+  p.dv = shared ? nullptr : (short *)a->dv;
   p.B = (int)a->B;
   p.Sq = (int)a->Sq;
   p.Skv = (int)a->Skv;
@@ -154,8 +160,13 @@ int attn_bwd_ex(const attn_bwd_args *a) {
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
     if (e == hipSuccess) e = attn::launch_sparse_dkdv(p, cnt, (int)skv_pad(a), dk_acc, dv_acc, bf16, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
-    if (e == hipSuccess) e = attn::launch_land(dk_acc, p.dk, nk, a->scale, bf16, st);
-    if (e == hipSuccess) e = attn::launch_land(dv_acc, p.dv, nv, 1.0f, bf16, st);
+    if (shared) {
+      if (e == hipSuccess)
+        e = attn::launch_land_kv(dk_acc, dv_acc, p.dk, a->B * a->Skv * a->Hkv, a->Dqk, a->Dv, a->scale, bf16, st);
+    } else {
+      if (e == hipSuccess) e = attn::launch_land(dk_acc, p.dk, nk, a->scale, bf16, st);
+      if (e == hipSuccess) e = attn::launch_land(dv_acc, p.dv, nv, 1.0f, bf16, st);
+    }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
   }
   if (!a->workspace) {

@@ -36,6 +36,8 @@ struct Params {
   const int32_t *idx;                 // [B,Sq,Hkv,topk] or null
   short *dq, *dk, *dv;
   int B, Sq, Skv, Hq, Hkv, G, topk, Dqk, Dv;
+  int v_ld;                           // elements between consecutive V rows: Dv, or Dqk when V is
+                                      // the first Dv columns of each K row (shared-latent form)
   int causal, window;
   float scale;                        // softmax scale
   float c;                            // scale * log2(e)

@@ -23,6 +23,7 @@ hipError_t launch_dense_dq(const Params &p, bool bf16, hipStream_t st);
 //   launch_sparse_dkdv key-owned dK/dV weighted by cnt, added into f32 accumulators
 //                      [B,Skv,Hkv,Dqk] / [B,Skv,Hkv,Dv];
 //   launch_land        out = storage(scale * acc) over n elements (n a multiple of 8).
+//   launch_land_kv     out [rows, Dqk] = storage(scale * dk_acc + [dv_acc, 0]) (shared-latent dKV).
 hipError_t launch_zero(float *buf, int64_t n, hipStream_t st);
 hipError_t launch_topk_count(const int32_t *idx, uint16_t *cnt, int64_t B, int64_t Sq, int64_t Skv, int64_t Hkv,
                              int64_t topk, int skv_pad, int causal, hipStream_t st);
@@ -30,5 +31,7 @@ hipError_t launch_sparse_dq(const Params &p, bool bf16, hipStream_t st);
 hipError_t launch_sparse_dkdv(const Params &p, const uint16_t *cnt, int skv_pad, float *dk_acc, float *dv_acc, bool bf16,
                               hipStream_t st);
 hipError_t launch_land(const float *acc, short *out, int64_t n, float scale, bool bf16, hipStream_t st);
+hipError_t launch_land_kv(const float *dk_acc, const float *dv_acc, short *out, int64_t rows, int64_t Dqk, int64_t Dv,
+                          float scale, bool bf16, hipStream_t st);
 
 }  // namespace attn

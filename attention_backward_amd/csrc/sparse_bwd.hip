@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
   // offset is row * Hkv * D * 2 (the host checks it fits 32 bits).
   const int64_t kv0 = (int64_t)b * p.Skv * p.Hkv + g, nkv = (int64_t)p.B * p.Skv * p.Hkv;
   const i4v rk = buf_rsrc(p.k + kv0 * DQK, (uint64_t)(nkv - kv0) * DQK * 2);
-  const i4v rv = buf_rsrc(p.v + kv0 * DV, (uint64_t)(nkv - kv0) * DV * 2);
+  const i4v rv = buf_rsrc(p.v + kv0 * p.v_ld, (uint64_t)(nkv - kv0) * p.v_ld * 2);
   auto gather = [&](int c) {
     const int buf = c & 1, sb = c % 3;
 #pragma unroll
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
 #pragma unroll
     for (int u = 0; u < C::KC * C::CV / 256; u++) {
       const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sp_sw<DV>(r);
-      b2lds16(rv, ((uint32_t)row_s[sb][r] * p.Hkv * DV + 8 * ch) * 2, &v_s[buf][(s - lane) * 8]);
+      b2lds16(rv, ((uint32_t)row_s[sb][r] * p.Hkv * p.v_ld + 8 * ch) * 2, &v_s[buf][(s - lane) * 8]);
     }
   };
   // B[k][n] = tile[row = 16*ks + 8*hi + e][col = 32*nb + lo] by transposed reads of a row-major
@@ -320,6 +320,32 @@ __global__ __launch_bounds__(256) void land_kernel(const float *__restrict__ acc
   }
 }
 
+// Shared-latent landing: dKV = DT(dK_acc * scale + [dV_acc, 0]).  Row r of dK_acc has c8k chunks
+// of 8 columns (Dqk / 8), row r of dV_acc c8v (Dv / 8); chunks past Dv take dK alone.
+template <class TT>
+__global__ __launch_bounds__(256) void land_kv_kernel(const float *__restrict__ dk_acc, const float *__restrict__ dv_acc,
+                                                      short *__restrict__ out, int64_t n8, int c8k, int c8v,
+                                                      float scale) {
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n8; v += (int64_t)gridDim.x * 256) {
+    const int64_t r = v / c8k;
+    const int c = (int)(v - r * c8k);
+    f4v a = *(const f4v *)&dk_acc[8 * v] * scale;
+    f4v b = *(const f4v *)&dk_acc[8 * v + 4] * scale;
+    if (c < c8v) {
+      const float *d = &dv_acc[8 * (r * c8v + c)];
+      a += *(const f4v *)d;
+      b += *(const f4v *)(d + 4);
+    }
+    s8v o;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      o[e] = TT::cvt(a[e]);
+      o[4 + e] = TT::cvt(b[e]);
+    }
+    *(s8v *)&out[8 * v] = o;
+  }
+}
+
 __global__ __launch_bounds__(256) void zero_kernel(float4 *__restrict__ buf, int64_t n4) {
   for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n4; v += (int64_t)gridDim.x * 256)
     buf[v] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -355,6 +381,22 @@ hipError_t launch_land(const float *acc, short *out, int64_t n, float scale, boo
     hipLaunchKernelGGL(land_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, acc, out, n8, scale);
   else
     hipLaunchKernelGGL(land_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, acc, out, n8, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_land_kv(const float *dk_acc, const float *dv_acc, short *out, int64_t rows, int64_t Dqk, int64_t Dv,
+                          float scale, bool bf16, hipStream_t st) {
+  if (Dqk % 8 != 0 || Dv % 8 != 0 || Dv > Dqk) return hipErrorInvalidValue;
+  const int64_t n8 = rows * (Dqk / 8);
+  int64_t blocks = (n8 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(land_kv_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, dk_acc, dv_acc, out, n8,
+                       (int)(Dqk / 8), (int)(Dv / 8), scale);
+  else
+    hipLaunchKernelGGL(land_kv_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, dk_acc, dv_acc, out, n8,
+                       (int)(Dqk / 8), (int)(Dv / 8), scale);
   return hipGetLastError();
 }
 

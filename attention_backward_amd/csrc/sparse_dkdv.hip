@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
 #pragma unroll
     for (int kk = 0; kk < C::KQ; kk++) kr[kk] = *(const s8v *)(p.k + r * DQK + 32 * kk + 8 * g16);
 #pragma unroll
-    for (int kk = 0; kk < C::KV; kk++) vr[kk] = *(const s8v *)(p.v + r * DV + 32 * kk + 8 * g16);
+    for (int kk = 0; kk < C::KV; kk++) vr[kk] = *(const s8v *)(p.v + r * p.v_ld + 32 * kk + 8 * g16);
   }
 
   // Accumulators (32 keys x 32-wide d blocks): dV blocks [4w, 4w+4), dK blocks [kf, kf + kn).

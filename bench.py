@@ -207,6 +207,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cold-iters", type=int, default=10)
+    ap.add_argument("--kv-shared", action="store_true",
+                    help="top-k workloads: the shared-latent form (V is the first Dv columns of K; one dKV output)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one fp16->f32 device copy reading this many MiB (a known-size "
                          "kernel against which profiler byte counters are scaled)")
@@ -220,14 +222,21 @@ def main():
     import attention_backward_amd as ab
 
     w = synth.WORKLOADS[args.workload]
+    shared = bool(args.kv_shared)
+    if shared and not w.topk:
+        print("--kv-shared applies to the top-k workloads only", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     inp = synth.make_inputs(w)
+    if shared:  # V is the first Dv columns of K
+        inp["v"] = inp["k"][..., : w.Dv].contiguous()
     q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
     idx = inp["idx"].to(dev) if w.topk else None
     o, lse = gpu_forward_inputs(q, k, v, w, idx)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    a = ab.make_args(q, k, v, o, do, lse, dq, dk, dv, scale=w.scale, causal=w.causal, window=w.window,
-                     topk_idx=idx)
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    dv = None if shared else torch.empty_like(v)
+    a = ab.make_args(q, k, None if shared else v, o, do, lse, dq, dk, dv, scale=w.scale, causal=w.causal,
+                     window=w.window, topk_idx=idx, kv_shared=shared)
     need = ab.attn_bwd_workspace_size(a)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), need
@@ -312,7 +321,7 @@ def main():
         main_flops = npairs * (4 * w.Dqk + 4 * w.Dv)
         main_tf = main_flops / (mean["sparse_dkdv"] * 1e-6) / 1e12
         acc_bytes = w.B * w.Skv * w.Hkv * (w.Dqk + w.Dv) * 4
-        land_bytes = acc_bytes + w.B * w.Skv * w.Hkv * (w.Dqk + w.Dv) * esz
+        land_bytes = acc_bytes + w.B * w.Skv * w.Hkv * (w.Dqk if shared else w.Dqk + w.Dv) * esz
         kernels = {
             "pre_and_dq": {"us": round(mean["pre_and_dq"], 2),
                            "note": "delta, zero-fill, key counts and the gathered dQ kernel"},
@@ -335,13 +344,15 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic: N(0,1) q,k,v,dO from a seeded PCG64 generator" +
                 ("; top-k lists of distinct causal keys drawn uniformly" if w.topk else "") +
+                ("; V = the first Dv columns of K (shared-latent form)" if shared else "") +
                 "; O and lse from an fp32 forward",
         "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal, "window": w.window, "topk": w.topk,
-                   "metric_flops": flops, "pairs": npairs},
+                   "kv_shared": shared, "metric_flops": flops, "pairs": npairs},
         "roofline": {"kernel": main_name, "bound": "mfma", "achieved": round(main_tf, 2),
                      "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(main_tf / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": profiled_traffic(main_name, w.name), "traffic_unit": "bytes per launch",
+                     "traffic": None if shared else profiled_traffic(main_name, w.name),
+                     "traffic_unit": "bytes per launch",
                      "algorithmic_flops_per_launch": main_flops},
         "kernels_us_median": {kname: round(v_, 2) for kname, v_ in med.items()},
         "kernels": kernels,

@@ -90,6 +90,12 @@ typedef struct {
                                        it, the zero-fill, the key counts and the dQ kernel |
                                        after the dK/dV kernel | after the landing passes
                                        (per-phase timing without changing the work)          */
+  int32_t kv_shared;                /* 0, or 1 for the shared-latent form of the top-k path (the
+                                       TileLang PR #2592 page's sparse MLA op, which returns dq and
+                                       dkv): k holds [B,Skv,Hkv,Dqk] rows whose first Dv columns are
+                                       V, v and dv must be NULL, and dk receives dKV = dK + [dV, 0],
+                                       the gradient with respect to that one tensor.  Requires
+                                       topk_idx and Dv <= Dqk.                                   */
 } attn_bwd_args;
 
 /* Bytes of workspace the call needs for these sizes (0 if the arguments are invalid), as
@@ -97,7 +103,8 @@ typedef struct {
  *   delta (stored negated) and a sanitised copy of lse, [B,Hq,Sq] f32 each;
  *   top-k only: f32 accumulators dK_acc [B,Skv,Hkv,Dqk] and dV_acc [B,Skv,Hkv,Dv].
  * Never an Hq-shaped dK/dV buffer.  Top-k results: dq is written once per element; dk and dv
- * are sums of f32 atomic additions, so their last bits may differ between identical calls. */
+ * (or dKV in the shared-latent form) are sums of f32 atomic additions, so their last bits may
+ * differ between identical calls.  The shared-latent form needs the same workspace. */
 size_t attn_bwd_workspace_size(const attn_bwd_args *a);
 
 /* The backward for the full argument set.  Returns an attn_status. */

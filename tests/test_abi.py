@@ -79,6 +79,12 @@ def test_workspace_size():
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, Skv=1 << 22, Hkv=1, Hq=64), -2),
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, workspace=0x100000, workspace_bytes=1 << 20), -3),
         (dict(workspace=0x100000, workspace_bytes=16), -3),
+        (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, kv_shared=2), -1),
+        (dict(kv_shared=1), -2),  # the shared-latent form exists on the top-k path only
+        (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, kv_shared=1), -1),  # v and dv must be NULL
+        # a valid shared-latent call up to the workspace check
+        (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, kv_shared=1, v=0, dv=0, workspace=0x100000,
+              workspace_bytes=16), -3),
         (dict(workspace=0x100080, workspace_bytes=1 << 30), -1),  # workspace not 256-byte aligned
         (dict(workspace=0, workspace_bytes=64), -1),
     ],

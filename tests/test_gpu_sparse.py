@@ -106,3 +106,70 @@ def test_sparse_full_size_sampled_parity():
     log(f"  {int((~sel).sum())} keys selected by no query")
     unsel = torch.from_numpy(~sel)
     assert torch.all(dk[0, unsel] == 0) and torch.all(dv[0, unsel] == 0)
+
+
+def prepare_shared(w):
+    """Inputs of the shared-latent form: V is the first Dv columns of K (O and lse from the forward
+    over that V)."""
+    import oracle.forward as oracle_forward
+
+    inp = synth.make_inputs(w)
+    inp["v"] = inp["k"][..., : w.Dv].contiguous()
+    if w.B * w.Sq * w.Skv * w.Hq <= 4 * 2 ** 20:
+        o, lse = oracle.fwd(inp["q"], inp["k"], inp["v"], w.scale, w.causal, w.window, inp["idx"].numpy())
+        inp["o"] = torch.from_numpy(o).to(synth.DTYPES[w.dtype])
+        inp["lse"] = torch.from_numpy(lse).to(torch.float32)
+    else:
+        inp["o"], inp["lse"] = oracle_forward.make_o_lse(w, inp)
+    return inp
+
+
+def run_shared(inp, w):
+    import attention_backward_amd as ab
+    from tests.helpers import poisoned_like, to_gpu
+
+    g = to_gpu(inp)
+    dq, dkv = poisoned_like(g["q"]), poisoned_like(g["k"])
+    args = ab.make_args(g["q"], g["k"], None, g["o"], g["dout"], g["lse"], dq, dkv, None, scale=w.scale,
+                        causal=w.causal, window=w.window, topk_idx=g["idx"], kv_shared=True)
+    need = ab.attn_bwd_workspace_size(args)
+    ws = poisoned_like(torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda"))
+    args.workspace, args.workspace_bytes = ws.data_ptr(), need
+    ab.attn_bwd_ex(args)
+    torch.cuda.synchronize()
+    return dq.cpu(), dkv.cpu()
+
+
+@pytest.mark.parametrize("w", SMALL[:2], ids=[w.name for w in SMALL[:2]])
+def test_sparse_shared_latent_parity(w):
+    """Shared-latent form (the TileLang PR #2592 page's sparse MLA op returns dq and dkv): one KV
+    tensor whose first Dv columns are V; dkv = dK + [dV, 0] of the oracle with V = KV[..., :Dv]."""
+    log(f"case {w.name} (shared latent)")
+    inp = prepare_shared(w)
+    dq, dkv = run_shared(inp, w)
+    rdq, rdk, rdv = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["o"], inp["dout"], inp["lse"], w.scale, w.causal,
+                               w.window, inp["idx"])
+    rdkv = rdk.copy()
+    rdkv[..., : w.Dv] += rdv
+    check_close("dq", dq.double().numpy(), rdq)
+    check_close("dkv", dkv.double().numpy(), rdkv)
+
+
+def test_sparse_shared_latent_full_size_sampled():
+    """The top-k workload in its shared-latent form, in the benchmark's launch configuration, on
+    sampled rows."""
+    w = W[C5]
+    log(f"case {C5} (shared latent, full size, sampled rows)")
+    inp = prepare_shared(w)
+    dq, dkv = run_shared(inp, w)
+    rng = np.random.default_rng(19)
+    qrows = sample_rows(rng, 24, w.B, w.Sq, w.Hq)
+    krows = sample_rows(rng, 24, w.B, w.Skv, w.Hkv, extra_i=(w.Skv - 3, w.Skv // 2))
+    args = (inp["q"], inp["k"], inp["v"], inp["o"], inp["dout"], inp["lse"], w.scale)
+    ref_dq = oracle.bwd_dq_rows(*args, qrows, w.causal, w.window, inp["idx"])
+    ref_dk, ref_dv = oracle.bwd_dkv_rows(*args, krows, w.causal, w.window, inp["idx"])
+    ref_dkv = ref_dk.copy()
+    ref_dkv[..., : w.Dv] += ref_dv
+    check_close("dq rows", dq[qrows[:, 0], qrows[:, 1], qrows[:, 2]].double().numpy(), ref_dq)
+    check_close("dkv rows", dkv[krows[:, 0], krows[:, 1], krows[:, 2]].double().numpy(), ref_dkv)
+    assert torch.isfinite(dq.float()).all() and torch.isfinite(dkv.float()).all()

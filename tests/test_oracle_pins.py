@@ -94,6 +94,35 @@ def test_finite_differences(c):
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, p, fd, an)
 
 
+def test_shared_latent_identity_by_finite_differences():
+    """Shared-latent form (the TileLang PR #2592 page's sparse MLA op returns dq and dkv: one KV
+    tensor whose first Dv columns are V): central differences of L(Q, KV) = sum(O(Q, KV, KV[..,
+    :Dv]) * dO) with respect to KV equal the oracle's dK + [dV, 0]."""
+    B, Sq, Skv, Hq, Hkv, Dqk, Dv = 1, 7, 9, 4, 1, 8, 6
+    q, kv, _, do = rnd(11, B, Sq, Skv, Hq, Hkv, Dqk, Dv)
+    idx = rnd_idx(12, B, Sq, Skv, Hkv, 6)
+    scale, causal = 1.0 / math.sqrt(Dqk), True
+    o, lse = oracle.fwd(q, kv, kv[..., :Dv].copy(), scale, causal, 0, idx)
+    dq, dk, dv = oracle.bwd(q, kv, kv[..., :Dv].copy(), o, do, lse, scale, causal, 0, idx)
+    dkv = dk.copy()
+    dkv[..., :Dv] += dv
+    h = 1e-6
+    flat = kv.reshape(-1)
+    for p in np.random.default_rng(13).choice(flat.size, size=32, replace=False):
+        keep = flat[p]
+        flat[p] = keep + h
+        lp = loss(q, kv, kv[..., :Dv].copy(), do, scale, causal, 0, idx)
+        flat[p] = keep - h
+        lm = loss(q, kv, kv[..., :Dv].copy(), do, scale, causal, 0, idx)
+        flat[p] = keep
+        fd = (lp - lm) / (2 * h)
+        an = dkv.reshape(-1)[p]
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (p, fd, an)
+    # both kinds of column are exercised: some with a dV part, some without
+    cols = np.random.default_rng(13).choice(flat.size, size=32, replace=False) % Dqk
+    assert (cols < Dv).any() and (cols >= Dv).any()
+
+
 def torch_autograd(q, k, v, do, scale, causal, window, idx):
     """Natural-base softmax attention with an explicit multiplicity mask, differentiated by torch."""
     B, Sq, Hq, _ = q.shape
