@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     attn_bwd_ex,
     attn_bwd_strerror,
     attn_bwd_workspace_size,
+    attn_fwd,
     load,
     make_args,
 )
@@ -48,3 +49,14 @@ def backward(q, k, v, o, dout, lse, *, causal=True, window=0, topk_idx=None, sca
         args.workspace, args.workspace_bytes = ws.data_ptr(), need
     attn_bwd_ex(args)
     return dq, dk, dv
+
+
+def forward(q, k, v, *, causal=True, window=0, scale=None, stream=None):
+    """Allocate o and lse (with torch) and run attn_fwd on the current stream: the O and base-2 lse
+    the backward takes."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, scale, causal=causal, window=window, stream=stream)
+    return o, lse

@@ -19,7 +19,8 @@ ATTN_DT_F16, ATTN_DT_BF16 = 0, 1
 ATTN_OK, ATTN_E_INVAL, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = 0, -1, -2, -3, -4
 _DT = {torch.float16: ATTN_DT_F16, torch.bfloat16: ATTN_DT_BF16}
 
-EXPORTS = ("attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_size", "attn_bwd_delta", "attn_bwd_strerror")
+EXPORTS = ("attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_size", "attn_bwd_delta", "attn_fwd",
+           "attn_bwd_strerror")
 
 
 class attn_bwd_args(ctypes.Structure):  # noqa: N801  (mirrors the C struct name)
@@ -67,6 +68,8 @@ def load() -> ctypes.CDLL:
         lib.attn_bwd.restype = ctypes.c_int
         lib.attn_bwd_delta.argtypes = [P, P, P, I64, I64, I64, I64, I32, P]
         lib.attn_bwd_delta.restype = ctypes.c_int
+        lib.attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, I32, I32, P]
+        lib.attn_fwd.restype = ctypes.c_int
         lib.attn_bwd_strerror.argtypes = [ctypes.c_int]
         lib.attn_bwd_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -161,3 +164,13 @@ def attn_bwd_delta(o, dout, delta, stream=None) -> None:
     dt = o.dtype
     _check(load().attn_bwd_delta(_dev(o, "o", dt), _dev(dout, "dout", dt), _dev(delta, "delta", torch.float32), B, Sq,
                                  Hq, Dv, _DT[dt], _stream(stream)))
+
+
+def attn_fwd(q, k, v, o, lse, scale, causal=True, window=0, stream=None) -> None:
+    """o [B,Sq,Hq,D] and lse [B,Hq,Sq] f32 (base 2) from q [B,Sq,Hq,D], k and v [B,Skv,Hkv,D]."""
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    dt = q.dtype
+    _check(load().attn_fwd(_dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _dev(o, "o", dt),
+                           _dev(lse, "lse", torch.float32), B, Sq, Skv, Hq, Hkv, D, float(scale), int(causal),
+                           int(window), _DT[dt], _stream(stream)))

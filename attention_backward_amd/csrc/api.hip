@@ -211,6 +211,38 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
   return attn_bwd_ex(&a);
 }
 
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t Sq, int64_t Skv,
+             int64_t Hq, int64_t Hkv, int64_t D, float scale, int32_t causal, int32_t window, int32_t dtype,
+             void *stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_E_INVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3) != 0) return ATTN_E_INVAL;
+  if (B < 1 || Sq < 1 || Skv < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv != 0) return ATTN_E_INVAL;
+  if ((causal != 0 && causal != 1) || window < 0 || (window > 0 && !causal)) return ATTN_E_INVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_E_INVAL;
+  if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16) return ATTN_E_INVAL;
+  if (D != 64 && D != 128) return ATTN_E_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;
+  if (B * Sq * Hq >= lim || B * Skv * Hkv >= lim) return ATTN_E_UNSUPPORTED;
+  attn::FwdParams p;
+  p.q = (const short *)q;
+  p.k = (const short *)k;
+  p.v = (const short *)v;
+  p.o = (short *)o;
+  p.lse = lse;
+  p.B = (int)B;
+  p.Sq = (int)Sq;
+  p.Skv = (int)Skv;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.G = (int)(Hq / Hkv);
+  p.causal = causal;
+  p.window = window;
+  p.c = (float)((double)scale * 1.4426950408889634);
+  const hipError_t e = attn::launch_dense_fwd(p, (int)D, dtype == ATTN_DT_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return set_hip_error(e, "kernel launch");
+  return ATTN_OK;
+}
+
 int attn_bwd_delta(const void *o, const void *dout, float *delta, int64_t B, int64_t Sq, int64_t Hq, int64_t Dv,
                    int32_t dtype, void *stream) {
   if (!o || !dout || !delta || !aligned16(o) || !aligned16(dout) || !aligned16(delta)) return ATTN_E_INVAL;

@@ -16,6 +16,19 @@ hipError_t launch_delta(const short *o, const short *dout, float *delta, const f
 hipError_t launch_dense_dkdv(const Params &p, bool bf16, hipStream_t st);
 hipError_t launch_dense_dq(const Params &p, bool bf16, hipStream_t st);
 
+// Arguments of the forward kernel (O and the base-2 lse from Q, K, V).
+struct FwdParams {
+  const short *q, *k, *v;  // element bits of fp16/bf16, BSHD
+  short *o;                // [B,Sq,Hq,D]
+  float *lse;              // [B,Hq,Sq], base 2
+  int B, Sq, Skv, Hq, Hkv, G;
+  int causal, window;
+  float c;                 // scale * log2(e)
+};
+
+// Forward (the step before the backward): O and the base-2 lse, D in {64, 128}.
+hipError_t launch_dense_fwd(const FwdParams &p, int D, bool bf16, hipStream_t st);
+
 // Top-k path, (Dqk, Dv) = (576, 512):
 //   launch_zero        zero-fills n floats (n a multiple of 4): the accumulators and count mask;
 //   launch_topk_count  cnt [B,Hkv,Sq,skv_pad] u16 = occurrences of each key in each valid list;

@@ -198,6 +198,56 @@ def cpu_baseline_topk(w, inp_cpu, target_s, threads):
             "seconds": dt}
 
 
+def bench_forward(args, w, ab):
+    """The forward alone: K back-to-back attn_fwd calls on resident q, k, v; one JSON line."""
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        ab.attn_fwd(q, k, v, o, lse, w.scale, causal=w.causal, window=w.window, stream=stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for s_ in range(args.steps):
+        ab.attn_fwd(q, k, v, o, lse, w.scale, causal=w.causal, window=w.window, stream=stream)
+        ev[s_ + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps)]
+    ms_per_step = wall * 1e3 / args.steps
+    npairs = pairs(w)
+    flops = npairs * (2 * w.Dqk + 2 * w.Dv)  # S = Q K^T and O = P V over the unmasked pairs
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    ktf = flops / (statistics.fmean(per) * 1e-6) / 1e12
+    result = {
+        "metric": "attn-fwd TFLOP/s (causal-adjusted) + % of MI355X fp16/bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: N(0,1) q,k,v from a seeded PCG64 generator",
+        "config": {"workload": w.name + " (forward)", "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal, "window": w.window, "metric_flops": flops,
+                   "pairs": npairs},
+        "roofline": {"kernel": "dense_fwd", "bound": "mfma", "achieved": round(ktf, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ktf / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops},
+        "kernels_us_median": {"fwd": round(statistics.median(per), 2)},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +259,8 @@ def main():
     ap.add_argument("--cold-iters", type=int, default=10)
     ap.add_argument("--kv-shared", action="store_true",
                     help="top-k workloads: the shared-latent form (V is the first Dv columns of K; one dKV output)")
+    ap.add_argument("--forward", action="store_true",
+                    help="dense workloads: time the forward kernel (O and lse from q, k, v) instead")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one fp16->f32 device copy reading this many MiB (a known-size "
                          "kernel against which profiler byte counters are scaled)")
@@ -226,6 +278,12 @@ def main():
     if shared and not w.topk:
         print("--kv-shared applies to the top-k workloads only", file=sys.stderr)
         sys.exit(2)
+    if args.forward:
+        if w.topk:
+            print("--forward covers the dense workloads only", file=sys.stderr)
+            sys.exit(2)
+        bench_forward(args, w, ab)
+        return
     dev = torch.device("cuda:0")
     inp = synth.make_inputs(w)
     if shared:  # V is the first Dv columns of K

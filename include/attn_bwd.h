@@ -125,6 +125,23 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
 int attn_bwd_delta(const void *o, const void *dout, float *delta, int64_t B, int64_t Sq, int64_t Hq, int64_t Dv,
                    int32_t dtype, void *stream);
 
+/* The forward pass whose outputs the backward consumes: o and the base-2 lse from q, k, v (the
+ * TileOPs PR #2281 page's Reference program defines lse over scores scaled by scale * log2(e)):
+ *   lse_i = log2 sum_j exp2(c q_i . k_j),  o_i = sum_j exp2(c q_i . k_j - lse_i) v_j,
+ *   c = scale * log2(e), over the keys j allowed to row i by the dense masks above (causal,
+ *   window; GQA head h reads KV head h / (Hq/Hkv)).  A row with no allowed key gets o = 0 and
+ *   lse = -inf.
+ * q [B,Sq,Hq,D], k and v [B,Skv,Hkv,D], o [B,Sq,Hq,D] of dtype with D in {64, 128} (other D:
+ * ATTN_E_UNSUPPORTED); lse [B,Hq,Sq] float32, 4-byte aligned; q, k, v, o 16-byte aligned device
+ * pointers owned by the caller.  Softmax statistics are kept in f32, P enters the O product in the
+ * element type.  Enqueued on `stream`, no workspace, no synchronisation; every element of o and
+ * lse is written.  Returns ATTN_E_INVAL for null or misaligned pointers, sizes < 1,
+ * Hq % Hkv != 0, causal not 0/1, window < 0, window > 0 without causal, scale not finite and
+ * positive, or an unknown dtype. */
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t Sq, int64_t Skv,
+             int64_t Hq, int64_t Hkv, int64_t D, float scale, int32_t causal, int32_t window, int32_t dtype,
+             void *stream);
+
 /* Static description of a status code (never NULL).  For ATTN_E_HIP the string includes the
  * HIP error text of the last failure on the calling thread. */
 const char *attn_bwd_strerror(int status);

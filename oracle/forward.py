@@ -98,6 +98,24 @@ def fwd(q, k, v, scale, causal=True, window=0, idx=None, dtype=torch.float64, ro
     return o, lse
 
 
+def fwd_rows(q, k, v, scale, rows, causal=True, window=0):
+    """The dense forward of single query rows: rows [n, 3] of (b, i, h) triples; returns
+    o [n, Dv] and lse [n] in f64, each row's softmax taken over its whole allowed key set."""
+    Sq, Hq, Skv, Hkv = q.shape[1], q.shape[2], k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    c = scale * LOG2E
+    o = torch.empty((len(rows), v.shape[3]), dtype=torch.float64)
+    lse = torch.empty((len(rows),), dtype=torch.float64)
+    for n, (b, i, h) in enumerate(rows):
+        b, i, h = int(b), int(i), int(h)
+        qq = q[b, i:i + 1, h, :].to(torch.float64)
+        kk = k[b, :, h // G, :].to(torch.float64)
+        vv = v[b, :, h // G, :].to(torch.float64)
+        oo, ll = _dense_rows(qq, kk, vv, i, i + 1, Skv - Sq, causal, window, c)
+        o[n], lse[n] = oo[0], ll[0]
+    return o, lse
+
+
 def make_o_lse(w, inputs, dtype=torch.float64):
     """O rounded to the workload's storage dtype and lse rounded to float32, from a forward pass
     over the drawn inputs.  Both sides of every comparison consume these same bytes."""

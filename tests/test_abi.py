@@ -107,6 +107,35 @@ def test_plain_entry_point_validates():
     assert rc == -2
 
 
+FWD_OK = dict(q=0x100000, k=0x100000, v=0x100000, o=0x100000, lse=0x100000, B=1, Sq=128, Skv=128, Hq=4, Hkv=2,
+              D=128, scale=0.088, causal=1, window=0, dtype=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1),
+    (dict(lse=None), -1),
+    (dict(o=0x100008), -1),          # not 16-byte aligned
+    (dict(lse=0x100002), -1),        # not 4-byte aligned
+    (dict(Sq=0), -1),
+    (dict(Skv=0), -1),
+    (dict(Hkv=3), -1),               # Hq % Hkv != 0
+    (dict(causal=2), -1),
+    (dict(window=-1), -1),
+    (dict(causal=0, window=8), -1),  # a window needs the causal mask
+    (dict(scale=0.0), -1),
+    (dict(scale=float("inf")), -1),
+    (dict(dtype=7), -1),
+    (dict(D=96), -2),
+    (dict(D=576), -2),
+])
+def test_forward_entry_point_validates(kw, status):
+    """Every case fails validation on the host, so no kernel is launched."""
+    a = dict(FWD_OK, **kw)
+    rc = ab.load().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Sq"], a["Skv"], a["Hq"], a["Hkv"],
+                            a["D"], a["scale"], a["causal"], a["window"], a["dtype"], None)
+    assert rc == status
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
 

@@ -330,6 +330,22 @@ def test_torch_forward_matches_c_forward(c):
     np.testing.assert_allclose(tl.numpy()[fin], lse[fin], rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("c", [c for c in CASES if not c[-1]])
+def test_forward_rows_match_c_forward(c):
+    """The single-row forward used for sampled checks at full size equals the C forward on every row."""
+    q, k, v, do, idx, scale, causal, window = case_inputs(c, seed=33)
+    o, lse = oracle.fwd(q, k, v, scale, causal, window, None)
+    B, Sq, Hq = q.shape[:3]
+    rows = np.array([(b, i, h) for b in range(B) for i in range(Sq) for h in range(Hq)])
+    t = lambda a: torch.from_numpy(a)  # noqa: E731
+    ro, rl = oracle_forward.fwd_rows(t(q), t(k), t(v), scale, rows, causal, window)
+    np.testing.assert_allclose(ro.numpy(), o.reshape(-1, v.shape[3]), rtol=1e-12, atol=1e-13)
+    want = lse.transpose(0, 2, 1).reshape(-1)
+    np.testing.assert_array_equal(np.isinf(rl.numpy()), np.isinf(want))
+    fin = np.isfinite(want)
+    np.testing.assert_allclose(rl.numpy()[fin], want[fin], rtol=1e-12, atol=1e-12)
+
+
 def test_lse_minus_inf_row_contributes_nothing():
     q, k, v, do = rnd(37, 1, 6, 6, 2, 2, 4, 4)
     o, lse = oracle.fwd(q, k, v, 0.5, True, 0)
