@@ -198,33 +198,53 @@ def cpu_baseline_topk(w, inp_cpu, target_s, threads):
             "seconds": dt}
 
 
-def bench_forward(args, w, ab):
-    """The forward alone: K back-to-back attn_fwd calls on resident q, k, v; one JSON line."""
+def bench_forward(args, w, ab, with_bwd=False):
+    """The forward alone (or forward + backward per step): K back-to-back calls on resident q, k, v
+    (and dO); one JSON line.  The roofline is the forward kernel's, from events around it."""
     dev = torch.device("cuda:0")
     inp = synth.make_inputs(w)
-    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    a = None
+    if with_bwd:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        a = ab.make_args(q, k, v, o, do, lse, dq, dk, dv, scale=w.scale, causal=w.causal, window=w.window)
+        need = ab.attn_bwd_workspace_size(a)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = ws.data_ptr(), need
+
+    def step():
+        ab.attn_fwd(q, k, v, o, lse, w.scale, causal=w.causal, window=w.window, stream=stream)
+        if with_bwd:
+            ab.attn_bwd_ex(a)
+
     for _ in range(args.warmup):
-        ab.attn_fwd(q, k, v, o, lse, w.scale, causal=w.causal, window=w.window, stream=stream)
+        step()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    ev[0].record(stream)
-    for s_ in range(args.steps):
+    for row in ev:
+        row[0].record(stream)
         ab.attn_fwd(q, k, v, o, lse, w.scale, causal=w.causal, window=w.window, stream=stream)
-        ev[s_ + 1].record(stream)
+        row[1].record(stream)
+        if with_bwd:
+            ab.attn_bwd_ex(a)
+        row[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps)]
+    per = [row[0].elapsed_time(row[1]) * 1e3 for row in ev]
+    per_b = [row[1].elapsed_time(row[2]) * 1e3 for row in ev]
     ms_per_step = wall * 1e3 / args.steps
     npairs = pairs(w)
-    flops = npairs * (2 * w.Dqk + 2 * w.Dv)  # S = Q K^T and O = P V over the unmasked pairs
+    fwd_flops = npairs * (2 * w.Dqk + 2 * w.Dv)  # S = Q K^T and O = P V over the unmasked pairs
+    flops = fwd_flops * (3.5 if with_bwd else 1.0)  # the backward counted as 2.5 forwards
     value = flops / (ms_per_step * 1e-3) / 1e12
-    ktf = flops / (statistics.fmean(per) * 1e-6) / 1e12
+    ktf = fwd_flops / (statistics.fmean(per) * 1e-6) / 1e12
+    what = "attn-fwd+bwd" if with_bwd else "attn-fwd"
     result = {
-        "metric": "attn-fwd TFLOP/s (causal-adjusted) + % of MI355X fp16/bf16 MFMA peak",
+        "metric": what + " TFLOP/s (causal-adjusted) + % of MI355X fp16/bf16 MFMA peak",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "pct_of_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
@@ -236,14 +256,15 @@ def bench_forward(args, w, ab):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic: N(0,1) q,k,v from a seeded PCG64 generator",
-        "config": {"workload": w.name + " (forward)", "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv,
+        "data": "synthetic: N(0,1) q,k,v" + (",dO" if with_bwd else "") + " from a seeded PCG64 generator",
+        "config": {"workload": w.name + (" (forward + backward)" if with_bwd else " (forward)"), "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal, "window": w.window, "metric_flops": flops,
                    "pairs": npairs},
         "roofline": {"kernel": "dense_fwd", "bound": "mfma", "achieved": round(ktf, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ktf / PEAK_MFMA_TFLOPS, 4), "traffic": None,
-                     "algorithmic_flops_per_launch": flops},
-        "kernels_us_median": {"fwd": round(statistics.median(per), 2)},
+                     "algorithmic_flops_per_launch": fwd_flops},
+        "kernels_us_median": {"fwd": round(statistics.median(per), 2)} |
+                             ({"bwd_call": round(statistics.median(per_b), 2)} if with_bwd else {}),
     }
     print(json.dumps(result), flush=True)
 
@@ -261,6 +282,8 @@ def main():
                     help="top-k workloads: the shared-latent form (V is the first Dv columns of K; one dKV output)")
     ap.add_argument("--forward", action="store_true",
                     help="dense workloads: time the forward kernel (O and lse from q, k, v) instead")
+    ap.add_argument("--fwd-bwd", action="store_true",
+                    help="dense workloads: time forward + backward per step (O and lse from the forward kernel)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one fp16->f32 device copy reading this many MiB (a known-size "
                          "kernel against which profiler byte counters are scaled)")
@@ -278,11 +301,11 @@ def main():
     if shared and not w.topk:
         print("--kv-shared applies to the top-k workloads only", file=sys.stderr)
         sys.exit(2)
-    if args.forward:
+    if args.forward or args.fwd_bwd:
         if w.topk:
-            print("--forward covers the dense workloads only", file=sys.stderr)
+            print("--forward and --fwd-bwd cover the dense workloads only", file=sys.stderr)
             sys.exit(2)
-        bench_forward(args, w, ab)
+        bench_forward(args, w, ab, with_bwd=args.fwd_bwd)
         return
     dev = torch.device("cuda:0")
     inp = synth.make_inputs(w)
