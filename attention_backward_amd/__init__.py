@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     attn_bwd_strerror,
     attn_bwd_workspace_size,
     attn_fwd,
+    attn_fwd_varlen,
     load,
     make_args,
 )

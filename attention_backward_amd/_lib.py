@@ -20,7 +20,7 @@ ATTN_OK, ATTN_E_INVAL, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = 0, -1,
 _DT = {torch.float16: ATTN_DT_F16, torch.bfloat16: ATTN_DT_BF16}
 
 EXPORTS = ("attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_size", "attn_bwd_delta", "attn_fwd",
-           "attn_bwd_strerror")
+           "attn_fwd_varlen", "attn_bwd_strerror")
 
 
 class attn_bwd_args(ctypes.Structure):  # noqa: N801  (mirrors the C struct name)
@@ -37,6 +37,7 @@ class attn_bwd_args(ctypes.Structure):  # noqa: N801  (mirrors the C struct name
         ("stream", ctypes.c_void_p),
         ("events", ctypes.c_void_p),
         ("kv_shared", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p), ("nseq", ctypes.c_int64), ("max_seqlen", ctypes.c_int64),
     ]
 
 
@@ -70,6 +71,9 @@ def load() -> ctypes.CDLL:
         lib.attn_bwd_delta.restype = ctypes.c_int
         lib.attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, I32, I32, P]
         lib.attn_fwd.restype = ctypes.c_int
+        lib.attn_fwd_varlen.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, I32,
+                                         I32, P]
+        lib.attn_fwd_varlen.restype = ctypes.c_int
         lib.attn_bwd_strerror.argtypes = [ctypes.c_int]
         lib.attn_bwd_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -104,11 +108,13 @@ def _stream(stream):
 
 
 def make_args(q, k, v, o, dout, lse, dq, dk, dv, *, scale, causal=True, window=0, topk_idx=None,
-              workspace=None, stream=None, kv_shared=False) -> attn_bwd_args:
+              workspace=None, stream=None, kv_shared=False, cu_seqlens=None, max_seqlen=None) -> attn_bwd_args:
     """Fill an attn_bwd_args from torch tensors (shapes taken from q [B,Sq,Hq,Dqk], k and dout).
 
     kv_shared: the shared-latent form of the top-k path; v and dv are None, V is the first Dv
-    columns of k and dk receives dK + [dV, 0]."""
+    columns of k and dk receives dK + [dV, 0].
+    cu_seqlens: packed sequences (int32 [nseq + 1] on the GPU; tensors [1, T, H, D]); max_seqlen,
+    a host int bounding every length, is then required."""
     if q.dtype not in _DT:
         raise TypeError(f"unsupported dtype {q.dtype}")
     if kv_shared and (v is not None or dv is not None):
@@ -124,6 +130,11 @@ def make_args(q, k, v, o, dout, lse, dq, dk, dv, *, scale, causal=True, window=0
     a.topk_idx = _dev(topk_idx, "topk_idx", torch.int32)
     a.dq, a.dk, a.dv = _dev(dq, "dq", dt), _dev(dk, "dk", dt), _dev(dv, "dv", dt)
     a.kv_shared = int(bool(kv_shared))
+    if cu_seqlens is not None:
+        if max_seqlen is None:
+            raise ValueError("cu_seqlens needs max_seqlen (a host int bounding every sequence length)")
+        a.cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32)
+        a.nseq, a.max_seqlen = cu_seqlens.numel() - 1, int(max_seqlen)
     a.B, a.Sq, a.Skv, a.Hq, a.Hkv, a.Dqk, a.Dv = B, Sq, Skv, Hq, Hkv, Dqk, Dv
     a.topk = 0 if topk_idx is None else topk_idx.shape[-1]
     a.scale = float(scale)
@@ -174,3 +185,15 @@ def attn_fwd(q, k, v, o, lse, scale, causal=True, window=0, stream=None) -> None
     _check(load().attn_fwd(_dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _dev(o, "o", dt),
                            _dev(lse, "lse", torch.float32), B, Sq, Skv, Hq, Hkv, D, float(scale), int(causal),
                            int(window), _DT[dt], _stream(stream)))
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, scale, causal=True, window=0, stream=None) -> None:
+    """The forward over packed sequences: q, o [1,T,Hq,D], k, v [1,T,Hkv,D], lse [1,Hq,T] f32,
+    cu_seqlens int32 [nseq + 1] on the GPU, max_seqlen a host int bounding every length."""
+    _, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    dt = q.dtype
+    _check(load().attn_fwd_varlen(_dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _dev(o, "o", dt),
+                                  _dev(lse, "lse", torch.float32), _dev(cu_seqlens, "cu_seqlens", torch.int32),
+                                  cu_seqlens.numel() - 1, int(max_seqlen), T, Hq, Hkv, D, float(scale), int(causal),
+                                  int(window), _DT[dt], _stream(stream)))

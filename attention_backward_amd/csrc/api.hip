@@ -42,6 +42,14 @@ int validate_sizes(const attn_bwd_args *a) {
   if (a->dtype != ATTN_DT_F16 && a->dtype != ATTN_DT_BF16) return ATTN_E_INVAL;
   if (a->kv_shared != 0 && a->kv_shared != 1) return ATTN_E_INVAL;
   if (a->kv_shared && !a->topk_idx) return ATTN_E_UNSUPPORTED;  // the dense kernels have no shared form
+  if (a->cu_seqlens) {
+    // Packed sequences: a batch of one on the dense path, each sequence its own problem.
+    if (((uintptr_t)a->cu_seqlens & 3) != 0 || a->B != 1 || a->Sq != a->Skv || a->topk_idx) return ATTN_E_INVAL;
+    if (a->nseq < 1 || a->max_seqlen < 1 || a->max_seqlen > a->Sq) return ATTN_E_INVAL;
+    if (a->nseq * a->Hq * a->max_seqlen >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;  // grid size
+  } else if (a->nseq != 0 || a->max_seqlen != 0) {
+    return ATTN_E_INVAL;
+  }
   // 32-bit row indices inside the kernels: every row count must fit comfortably.
   const int64_t lim = (int64_t)1 << 31;
   if (a->B * a->Sq * a->Hq >= lim || a->B * a->Skv * a->Hkv >= lim) return ATTN_E_UNSUPPORTED;
@@ -68,6 +76,43 @@ size_t workspace_bytes_for(const attn_bwd_args *a) {
   size_t n = 2 * row_stat_bytes(a);
   if (a->topk_idx) n += dk_acc_bytes(a) + dv_acc_bytes(a) + cnt_bytes(a);
   return n;
+}
+
+// The forward for dense batches (cu null) and packed sequences (cu set: B = 1, Sq = Skv = T).
+int run_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t Sq, int64_t Skv,
+            int64_t Hq, int64_t Hkv, int64_t D, float scale, int32_t causal, int32_t window, int32_t dtype,
+            const int32_t *cu, int64_t nseq, int64_t max_seqlen, void *stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_E_INVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3) != 0) return ATTN_E_INVAL;
+  if (B < 1 || Sq < 1 || Skv < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv != 0) return ATTN_E_INVAL;
+  if ((causal != 0 && causal != 1) || window < 0 || (window > 0 && !causal)) return ATTN_E_INVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_E_INVAL;
+  if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16) return ATTN_E_INVAL;
+  if (D != 64 && D != 128) return ATTN_E_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;
+  if (B * Sq * Hq >= lim || B * Skv * Hkv >= lim) return ATTN_E_UNSUPPORTED;
+  if (cu && nseq * Hq * max_seqlen >= lim) return ATTN_E_UNSUPPORTED;  // grid size
+  attn::FwdParams p;
+  p.q = (const short *)q;
+  p.k = (const short *)k;
+  p.v = (const short *)v;
+  p.o = (short *)o;
+  p.lse = lse;
+  p.B = (int)B;
+  p.Sq = (int)Sq;
+  p.Skv = (int)Skv;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.G = (int)(Hq / Hkv);
+  p.causal = causal;
+  p.window = window;
+  p.c = (float)((double)scale * 1.4426950408889634);
+  p.cu = cu;
+  p.nseq = (int)nseq;
+  p.max_seqlen = (int)max_seqlen;
+  const hipError_t e = attn::launch_dense_fwd(p, (int)D, dtype == ATTN_DT_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return set_hip_error(e, "kernel launch");
+  return ATTN_OK;
 }
 
 }  // namespace
@@ -134,6 +179,9 @@ int attn_bwd_ex(const attn_bwd_args *a) {
 
   p.lse_in = a->lse;
   p.lse_ws = (float *)p.lse;
+  p.cu = a->cu_seqlens;
+  p.nseq = (int)a->nseq;
+  p.max_seqlen = (int)a->max_seqlen;
 
   hipEvent_t *ev = (hipEvent_t *)a->events;
   hipError_t e = ev ? hipEventRecord(ev[0], st) : hipSuccess;
@@ -214,33 +262,16 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t Sq, int64_t Skv,
              int64_t Hq, int64_t Hkv, int64_t D, float scale, int32_t causal, int32_t window, int32_t dtype,
              void *stream) {
-  if (!q || !k || !v || !o || !lse) return ATTN_E_INVAL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3) != 0) return ATTN_E_INVAL;
-  if (B < 1 || Sq < 1 || Skv < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv != 0) return ATTN_E_INVAL;
-  if ((causal != 0 && causal != 1) || window < 0 || (window > 0 && !causal)) return ATTN_E_INVAL;
-  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_E_INVAL;
-  if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16) return ATTN_E_INVAL;
-  if (D != 64 && D != 128) return ATTN_E_UNSUPPORTED;
-  const int64_t lim = (int64_t)1 << 31;
-  if (B * Sq * Hq >= lim || B * Skv * Hkv >= lim) return ATTN_E_UNSUPPORTED;
-  attn::FwdParams p;
-  p.q = (const short *)q;
-  p.k = (const short *)k;
-  p.v = (const short *)v;
-  p.o = (short *)o;
-  p.lse = lse;
-  p.B = (int)B;
-  p.Sq = (int)Sq;
-  p.Skv = (int)Skv;
-  p.Hq = (int)Hq;
-  p.Hkv = (int)Hkv;
-  p.G = (int)(Hq / Hkv);
-  p.causal = causal;
-  p.window = window;
-  p.c = (float)((double)scale * 1.4426950408889634);
-  const hipError_t e = attn::launch_dense_fwd(p, (int)D, dtype == ATTN_DT_BF16, (hipStream_t)stream);
-  if (e != hipSuccess) return set_hip_error(e, "kernel launch");
-  return ATTN_OK;
+  return run_fwd(q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, scale, causal, window, dtype, nullptr, 0, 0, stream);
+}
+
+int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse, const int32_t *cu_seqlens,
+                    int64_t nseq, int64_t max_seqlen, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                    int32_t causal, int32_t window, int32_t dtype, void *stream) {
+  if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3) != 0) return ATTN_E_INVAL;
+  if (nseq < 1 || max_seqlen < 1 || max_seqlen > T) return ATTN_E_INVAL;
+  return run_fwd(q, k, v, o, lse, 1, T, T, Hq, Hkv, D, scale, causal, window, dtype, cu_seqlens, nseq, max_seqlen,
+                 stream);
 }
 
 int attn_bwd_delta(const void *o, const void *dout, float *delta, int64_t B, int64_t Sq, int64_t Hq, int64_t Dv,

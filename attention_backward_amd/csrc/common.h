@@ -41,7 +41,36 @@ struct Params {
   int causal, window;
   float scale;                        // softmax scale
   float c;                            // scale * log2(e)
+  const int32_t *cu;                  // packed sequences: [nseq + 1] token offsets, or null
+  int nseq, max_seqlen;               // packed sequences: their number and a bound on each length
 };
+
+// The sequence one workgroup works on.  Dense: batch s of equal-length sequences.  Packed (cu not
+// null, batch of one): tokens [cu[s], cu[s+1]) of the token axis, with Sq = Skv = T.  Offsets are
+// clamped into [0, T] and lengths to max_seqlen, so no offset table can move an access out of its
+// buffer.  lse/delta index of (head h, row i): l0 + h * Sq_total + i.
+struct SeqView {
+  int64_t q0, k0;  // token index of row 0 of the query and the key rows
+  int64_t l0;
+  int Sq, Skv;
+};
+__device__ __forceinline__ SeqView seq_view(const int32_t *cu, int s, int Sq_total, int Skv_total, int Hq,
+                                            int max_seqlen) {
+  SeqView v;
+  if (cu) {
+    const int bos = min(max(__builtin_amdgcn_readfirstlane(cu[s]), 0), Sq_total);
+    const int eos = min(max(__builtin_amdgcn_readfirstlane(cu[s + 1]), bos), Sq_total);
+    v.q0 = v.k0 = v.l0 = bos;
+    v.Sq = v.Skv = min(eos - bos, max_seqlen);
+  } else {
+    v.q0 = (int64_t)s * Sq_total;
+    v.k0 = (int64_t)s * Skv_total;
+    v.l0 = (int64_t)s * Hq * Sq_total;
+    v.Sq = Sq_total;
+    v.Skv = Skv_total;
+  }
+  return v;
+}
 
 // SPLIT: whether P and dS enter their MFMA products (dV += P^T dO, dK += dS^T Q, dQ += dS K) as
 // hi + lo halves.  bf16 keeps 8 mantissa bits, so one rounding costs up to 2^-9 relative per

@@ -57,21 +57,27 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5, lo = lane & 31;
   const int i16 = lane & 15, g16 = lane >> 4;
-  const int BH = p.B * p.Hq;
-  const int bh = blockIdx.x % BH, qbr = blockIdx.x / BH;
-  const int nqb = (p.Sq + C::BQ - 1) / C::BQ;
+  const int BH = (p.cu ? p.nseq : p.B) * p.Hq;
+  const int qbr = blockIdx.x / BH;
+  // Packed sequences without a window: rotate the (sequence, head) index by the query block so
+  // that one long sequence's blocks spread over the 8 XCDs (workgroups go round-robin over them).
+  const int bh = (blockIdx.x % BH + (p.cu && p.window == 0 ? qbr : 0)) % BH;
+  const int nqb = ((p.cu ? p.max_seqlen : p.Sq) + C::BQ - 1) / C::BQ;
   const int q0 = (nqb - 1 - qbr) * C::BQ;
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G;
+  const SeqView sv = seq_view(p.cu, b, p.Sq, p.Skv, p.Hq, p.max_seqlen);
+  const int Sq = sv.Sq, Skv = sv.Skv;
+  if (q0 >= Sq) return;  // a packed sequence shorter than the longest (whole workgroup)
   const int qw0 = q0 + 32 * w;
-  const int off = p.Skv - p.Sq;
+  const int off = Skv - Sq;
 
   // This wave's Q and dO rows as B operands B[k=d][n=query]; lse, delta and the allowed key
   // range [klo, khi] of the lane's query column.
   s8v qf[C::KK], dof[C::KK];
   const int qi = qw0 + lo;
-  const bool qok = qi < p.Sq;
+  const bool qok = qi < Sq;
   {
-    const int64_t o64 = ((int64_t)(b * p.Sq + (qok ? qi : 0)) * p.Hq + h) * D + 8 * hi;
+    const int64_t o64 = ((sv.q0 + (qok ? qi : 0)) * p.Hq + h) * D + 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < C::KK; kk++) {
       qf[kk] = qok ? *(const s8v *)(p.q + o64 + 16 * kk) : s8v{};
@@ -82,10 +88,10 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   // (split over the two lane halves like the dO operand; one cross-half add completes it) and lse
   // with -inf mapped to +inf.  Both also go to the workspace (delta negated) for the dK/dV
   // kernel, which runs after this one.
-  const int64_t li = ((int64_t)b * p.Hq + h) * p.Sq + (qok ? qi : 0);
+  const int64_t li = sv.l0 + (int64_t)h * p.Sq + (qok ? qi : 0);
   float dsum = 0.f;
   if (qok) {
-    const short *orow = p.o + ((int64_t)(b * p.Sq + qi) * p.Hq + h) * D + 8 * hi;
+    const short *orow = p.o + ((sv.q0 + qi) * p.Hq + h) * D + 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < C::KK; kk++) {
       const s8v ov = *(const s8v *)(orow + 16 * kk);
@@ -105,21 +111,21 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
 #pragma unroll
   for (int r = 0; r < 16; r++) ndr16[r] = ndr;
   const int klo = p.window > 0 ? qi + off - p.window + 1 : 0;
-  const int khi = !qok ? klo - 1 : p.causal ? min(qi + off, p.Skv - 1) : p.Skv - 1;
+  const int khi = !qok ? klo - 1 : p.causal ? min(qi + off, Skv - 1) : Skv - 1;
 
   f16v acc[C::ND];  // dQ rows of this wave's 32 queries, [32-wide d block]
 #pragma unroll
   for (int dn = 0; dn < C::ND; dn++) acc[dn] = f16v{};
 
   // Keys any row of this workgroup can see.
-  const int qlast = min(q0 + C::BQ, p.Sq) - 1;
-  int k_lo = 0, k_hi = p.Skv;
+  const int qlast = min(q0 + C::BQ, Sq) - 1;
+  int k_lo = 0, k_hi = Skv;
   if (p.window > 0) k_lo = max(0, q0 + off - p.window + 1);
-  if (p.causal) k_hi = min(p.Skv, qlast + off + 1);
+  if (p.causal) k_hi = min(Skv, qlast + off + 1);
   const int kb_lo = k_lo / BK;
   const int kb_hi = k_hi > k_lo ? (k_hi + BK - 1) / BK : kb_lo;
   const int nsteps = kb_hi - kb_lo;
-  const int wlast = min(qw0 + 32, p.Sq) - 1;  // last valid query row of this wave
+  const int wlast = min(qw0 + 32, Sq) - 1;  // last valid query row of this wave
 
   // Direct global->LDS tile loads: slot s of a tile is physical chunk s % CPR of row s / CPR and
   // holds logical chunk (s % CPR) ^ swz<D>(row).  Rows past the end are clamped to the last key
@@ -130,8 +136,8 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
     const int u = part >> 1;
     const int slot0 = (w * C::WIW + u) * 64;
     const int s = slot0 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz<D>(row);
-    const int kj = min(k0 + row, p.Skv - 1);
-    const int64_t o64 = ((int64_t)(b * p.Skv + kj) * p.Hkv + g) * D + 8 * ch;
+    const int kj = min(k0 + row, Skv - 1);
+    const int64_t o64 = ((sv.k0 + kj) * p.Hkv + g) * D + 8 * ch;
     if (part & 1)
       g2lds16(p.v + o64, &kv_s[buf][1][slot0 * 8]);
     else
@@ -173,12 +179,12 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   for (int t = 0; t < nsteps; t++) {
     const int buf = t & 1;
     const int k0 = (kb_lo + t) * BK;
-    const bool active = qw0 < p.Sq && (!p.causal || k0 <= wlast + off) &&
+    const bool active = qw0 < Sq && (!p.causal || k0 <= wlast + off) &&
                         (p.window <= 0 || k0 + BK - 1 > qw0 + off - p.window);
     if (t + 1 < nsteps) issue(t + 1, buf ^ 1);
     if (active) {
       const bool full = (!p.causal || k0 + BK - 1 <= qw0 + off) && (p.window <= 0 || k0 > qw0 + 31 + off - p.window) &&
-                        (k0 + BK <= p.Skv) && (qw0 + 32 <= p.Sq);
+                        (k0 + BK <= Skv) && (qw0 + 32 <= Sq);
       const short *ks = kv_s[buf][0];
       // Read bases of this step's tile for the natural K/V reads; the sub-block and row-block
       // offsets fold into the reads' offset fields.
@@ -280,8 +286,8 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     const int qr = qw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-    if (qr < p.Sq) {
-      short *row = p.dq + ((int64_t)(b * p.Sq + qr) * p.Hq + h) * D + lo;
+    if (qr < Sq) {
+      short *row = p.dq + ((sv.q0 + qr) * p.Hq + h) * D + lo;
 #pragma unroll
       for (int dn = 0; dn < C::ND; dn++) row[32 * dn] = TT::cvt(acc[dn][r] * p.scale);
     }
@@ -290,8 +296,8 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
 
 template <class TT, int D, int BK, int SB>
 static hipError_t launch_dq_t(const Params &p, hipStream_t st) {
-  const int nqb = (p.Sq + DqCfg<D, BK, SB>::BQ - 1) / DqCfg<D, BK, SB>::BQ;
-  const int64_t blocks = (int64_t)nqb * p.B * p.Hq;
+  const int nqb = ((p.cu ? p.max_seqlen : p.Sq) + DqCfg<D, BK, SB>::BQ - 1) / DqCfg<D, BK, SB>::BQ;
+  const int64_t blocks = (int64_t)nqb * (p.cu ? p.nseq : p.B) * p.Hq;
   if (blocks < 1) return hipSuccess;
   hipLaunchKernelGGL((dense_dq_kernel<TT, D, BK, SB>), dim3((unsigned)blocks), dim3(512), 0, st, p);
   return hipGetLastError();

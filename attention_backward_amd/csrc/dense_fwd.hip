@@ -49,26 +49,32 @@ __global__ __launch_bounds__(512, 1) void dense_fwd_kernel(const FwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5, lo = lane & 31;
   const int i16 = lane & 15, g16 = lane >> 4;
-  const int BH = p.B * p.Hq;
-  const int bh = blockIdx.x % BH, qbr = blockIdx.x / BH;
-  const int nqb = (p.Sq + C::BQ - 1) / C::BQ;
+  const int BH = (p.cu ? p.nseq : p.B) * p.Hq;
+  const int qbr = blockIdx.x / BH;
+  // Packed sequences without a window: rotate the (sequence, head) index by the query block so
+  // that one long sequence's blocks spread over the 8 XCDs (workgroups go round-robin over them).
+  const int bh = (blockIdx.x % BH + (p.cu && p.window == 0 ? qbr : 0)) % BH;
+  const int nqb = ((p.cu ? p.max_seqlen : p.Sq) + C::BQ - 1) / C::BQ;
   const int q0 = (nqb - 1 - qbr) * C::BQ;  // longest first under a causal mask
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G;
+  const SeqView sv = seq_view(p.cu, b, p.Sq, p.Skv, p.Hq, p.max_seqlen);
+  const int Sq = sv.Sq, Skv = sv.Skv;
+  if (q0 >= Sq) return;  // a packed sequence shorter than the longest (whole workgroup)
   const int qw0 = q0 + 32 * w;
-  const int off = p.Skv - p.Sq;
+  const int off = Skv - Sq;
 
   // This wave's Q rows as B operands B[k=d][n=query] and the allowed key range [klo, khi] of the
   // lane's query column.
   s8v qf[C::KK];
   const int qi = qw0 + lo;
-  const bool qok = qi < p.Sq;
+  const bool qok = qi < Sq;
   {
-    const int64_t o64 = ((int64_t)(b * p.Sq + (qok ? qi : 0)) * p.Hq + h) * D + 8 * hi;
+    const int64_t o64 = ((sv.q0 + (qok ? qi : 0)) * p.Hq + h) * D + 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < C::KK; kk++) qf[kk] = qok ? *(const s8v *)(p.q + o64 + 16 * kk) : s8v{};
   }
   const int klo = p.window > 0 ? qi + off - p.window + 1 : 0;
-  const int khi = !qok ? klo - 1 : p.causal ? min(qi + off, p.Skv - 1) : p.Skv - 1;
+  const int khi = !qok ? klo - 1 : p.causal ? min(qi + off, Skv - 1) : Skv - 1;
 
   // O^T accumulators: block dn, register r is d = 32 dn + 8 (r/4) + 4 hi + r%4, lane lo the query.
   f16v acc[C::ND];
@@ -78,14 +84,14 @@ __global__ __launch_bounds__(512, 1) void dense_fwd_kernel(const FwdParams p) {
   float l_run = 0.f;  // sum of 2^(s c - m_run) over this lane half's keys
 
   // Keys any row of this workgroup can see.
-  const int qlast = min(q0 + C::BQ, p.Sq) - 1;
-  int k_lo = 0, k_hi = p.Skv;
+  const int qlast = min(q0 + C::BQ, Sq) - 1;
+  int k_lo = 0, k_hi = Skv;
   if (p.window > 0) k_lo = max(0, q0 + off - p.window + 1);
-  if (p.causal) k_hi = min(p.Skv, qlast + off + 1);
+  if (p.causal) k_hi = min(Skv, qlast + off + 1);
   const int kb_lo = k_lo / BK;
   const int kb_hi = k_hi > k_lo ? (k_hi + BK - 1) / BK : kb_lo;
   const int nsteps = kb_hi - kb_lo;
-  const int wlast = min(qw0 + 32, p.Sq) - 1;
+  const int wlast = min(qw0 + 32, Sq) - 1;
 
   // Direct global->LDS tile loads: slot s of a tile is physical chunk s % CPR of row s / CPR and
   // holds logical chunk (s % CPR) ^ swz<D>(row).  Rows past the end are clamped to the last key
@@ -96,8 +102,8 @@ __global__ __launch_bounds__(512, 1) void dense_fwd_kernel(const FwdParams p) {
     for (int u = 0; u < C::WIW; u++) {
       const int slot0 = (w * C::WIW + u) * 64;
       const int s = slot0 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz<D>(row);
-      const int kj = min(k0 + row, p.Skv - 1);
-      const int64_t o64 = ((int64_t)(b * p.Skv + kj) * p.Hkv + g) * D + 8 * ch;
+      const int kj = min(k0 + row, Skv - 1);
+      const int64_t o64 = ((sv.k0 + kj) * p.Hkv + g) * D + 8 * ch;
       g2lds16(p.k + o64, &kv_s[buf][0][slot0 * 8]);
       g2lds16(p.v + o64, &kv_s[buf][1][slot0 * 8]);
     }
@@ -126,12 +132,12 @@ __global__ __launch_bounds__(512, 1) void dense_fwd_kernel(const FwdParams p) {
   for (int t = 0; t < nsteps; t++) {
     const int buf = t & 1;
     const int k0 = (kb_lo + t) * BK;
-    const bool active = qw0 < p.Sq && (!p.causal || k0 <= wlast + off) &&
+    const bool active = qw0 < Sq && (!p.causal || k0 <= wlast + off) &&
                         (p.window <= 0 || k0 + BK - 1 > qw0 + off - p.window);
     if (t + 1 < nsteps) issue(t + 1, buf ^ 1);
     if (active) {
       const bool full = (!p.causal || k0 + BK - 1 <= qw0 + off) && (p.window <= 0 || k0 > qw0 + 31 + off - p.window) &&
-                        (k0 + BK <= p.Skv) && (qw0 + 32 <= p.Sq);
+                        (k0 + BK <= Skv) && (qw0 + 32 <= Sq);
       uint32_t abk[C::KK];
 #pragma unroll
       for (int kk = 0; kk < C::KK; kk++) abk[kk] = lds_base_add(lds_addr(kv_s[buf][0]), nat_lane[kk]);
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(512, 1) void dense_fwd_kernel(const FwdParams p) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qok) {
-    short *row = p.o + ((int64_t)(b * p.Sq + qi) * p.Hq + h) * D + 4 * hi;
+    short *row = p.o + ((sv.q0 + qi) * p.Hq + h) * D + 4 * hi;
 #pragma unroll
     for (int dn = 0; dn < C::ND; dn++)
 #pragma unroll
@@ -231,14 +237,14 @@ __global__ __launch_bounds__(512, 1) void dense_fwd_kernel(const FwdParams p) {
         *(s4v *)&row[32 * dn + 8 * j] = v;
       }
     if (hi == 0)
-      p.lse[((int64_t)b * p.Hq + h) * p.Sq + qi] = l_tot > 0.f ? m_run + __builtin_amdgcn_logf(l_tot) : -__builtin_inff();
+      p.lse[sv.l0 + (int64_t)h * p.Sq + qi] = l_tot > 0.f ? m_run + __builtin_amdgcn_logf(l_tot) : -__builtin_inff();
   }
 }
 
 template <class TT, int D, int BK>
 static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t st) {
-  const int nqb = (p.Sq + FwdCfg<D, BK>::BQ - 1) / FwdCfg<D, BK>::BQ;
-  const int64_t blocks = (int64_t)nqb * p.B * p.Hq;
+  const int nqb = ((p.cu ? p.max_seqlen : p.Sq) + FwdCfg<D, BK>::BQ - 1) / FwdCfg<D, BK>::BQ;
+  const int64_t blocks = (int64_t)nqb * (p.cu ? p.nseq : p.B) * p.Hq;
   if (blocks < 1) return hipSuccess;
   hipLaunchKernelGGL((dense_fwd_kernel<TT, D, BK>), dim3((unsigned)blocks), dim3(512), 0, st, p);
   return hipGetLastError();

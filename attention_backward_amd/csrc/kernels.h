@@ -24,6 +24,8 @@ struct FwdParams {
   int B, Sq, Skv, Hq, Hkv, G;
   int causal, window;
   float c;                 // scale * log2(e)
+  const int32_t *cu;       // packed sequences: [nseq + 1] token offsets, or null
+  int nseq, max_seqlen;
 };
 
 // Forward (the step before the backward): O and the base-2 lse, D in {64, 128}.

@@ -11,6 +11,9 @@ Recipe (one numpy PCG64 generator per workload):
     distinct key indices drawn uniformly without replacement from the keys that query may
     see under bottom-right causal alignment, [0, i + Skv - Sq], kept in draw order, int32;
   * scale = 1 / sqrt(Dqk).
+  * packed variable-length workloads: first the sequence lengths (nseq - 1 distinct cut points
+    drawn uniformly from 1..T-1, sorted, so every length is at least 1 and they sum to T), then
+    q, k, v, dout as above in the batch-of-one shape [1, T, H, D].
 O and lse are not drawn: they are outputs of a forward pass over these inputs.
 """
 from __future__ import annotations
@@ -118,3 +121,54 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     if w.topk:
         out["idx"] = torch.from_numpy(draw_topk(rng, w.B, w.Sq, w.Skv, w.Hkv, w.topk, w.causal))
     return out
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """Packed variable-length sequences: T tokens in nseq sequences, dense masks inside each."""
+    name: str
+    T: int
+    nseq: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    causal: bool
+    window: int
+    seed: int
+    lens: tuple = ()  # fixed lengths (summing to T) instead of drawn ones
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+# The packed unequal-length GQA endpoint of the flash-linear-attention issue (flattened total
+# 16384, Hq 32 / Hkv 4, D 128, bf16), here ungated; the sliding-window variant at D 64.
+VARLEN_WORKLOADS = {
+    w.name: w
+    for w in [
+        VarlenWorkload("varlen_gqa_t16384_n8_hq32_hkv4_d128_bf16", 16384, 8, 32, 4, 128, "bf16", True, 0, 7),
+        VarlenWorkload("varlen_swa_gqa_t8192_n5_hq32_hkv4_d64_w512_bf16", 8192, 5, 32, 4, 64, "bf16", True, 512, 8),
+    ]
+}
+
+
+def draw_seqlens(rng: np.random.Generator, T: int, nseq: int) -> np.ndarray:
+    """nseq lengths >= 1 summing to T: the gaps between nseq - 1 distinct sorted cut points."""
+    cuts = np.sort(rng.choice(np.arange(1, T), size=nseq - 1, replace=False)) if nseq > 1 else np.array([], np.int64)
+    return np.diff(np.concatenate([[0], cuts, [T]])).astype(np.int64)
+
+
+def make_varlen_inputs(w: VarlenWorkload) -> dict:
+    """Lengths (drawn unless fixed), cu_seqlens (int32 [nseq + 1]) and q, k, v, dout [1, T, H, D]."""
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    lens = np.asarray(w.lens, np.int64) if w.lens else draw_seqlens(rng, w.T, w.nseq)
+    assert lens.sum() == w.T and lens.size == w.nseq
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = rng.standard_normal((1, w.T, w.Hq, w.D), dtype=np.float32)
+    k = rng.standard_normal((1, w.T, w.Hkv, w.D), dtype=np.float32)
+    v = rng.standard_normal((1, w.T, w.Hkv, w.D), dtype=np.float32)
+    do = rng.standard_normal((1, w.T, w.Hq, w.D), dtype=np.float32)
+    return {"q": round_to(q, w.dtype), "k": round_to(k, w.dtype), "v": round_to(v, w.dtype),
+            "dout": round_to(do, w.dtype), "cu": torch.from_numpy(cu), "max_seqlen": int(lens.max())}

@@ -40,11 +40,11 @@ METRIC = "attn-bwd TFLOP/s (causal-adjusted) + % of MI355X fp16/bf16 MFMA peak"
 # files at the time: once the sources change, the figure no longer applies and is reported as null.
 PROFILED_TRAFFIC = {
     ("dense_dkdv", "mha_causal_b2_s2048_h32_d128_fp16"): dict(
-        fetch_kib=111308.4, write_kib=65536.0, fetch_scale=2.000, write_scale=1.000,
-        files=("dense_dkdv.hip", "common.h"), sha="5f1bb3e3d5528951"),
+        fetch_kib=112138.8, write_kib=65536.0, fetch_scale=2.000, write_scale=1.000,
+        files=("dense_dkdv.hip", "common.h"), sha="b1068c31a18d0977"),
     ("sparse_dkdv", "sparse_mla_b1_sq4096_skv8192_h64_dqk576_dv512_top2048_bf16"): dict(
-        fetch_kib=7482968.2, write_kib=217600.0, fetch_scale=2.000, write_scale=1.000,
-        files=("sparse_dkdv.hip", "common.h"), sha="1b72654de7750b0a"),
+        fetch_kib=7479495.5, write_kib=217600.0, fetch_scale=2.000, write_scale=1.000,
+        files=("sparse_dkdv.hip", "common.h"), sha="552775905fa59087"),
 }
 
 
@@ -269,12 +269,111 @@ def bench_forward(args, w, ab, with_bwd=False):
     print(json.dumps(result), flush=True)
 
 
+def varlen_pairs(vw, lens) -> int:
+    """Unmasked (query, key, head) pairs of packed sequences: each sequence's dense count."""
+    return sum(pairs(synth.Workload("", 1, int(n), int(n), vw.Hq, vw.Hkv, vw.D, vw.D, vw.dtype, vw.causal, vw.window,
+                                    0, 0)) for n in lens if n > 0)
+
+
+def bench_varlen(args, vw, ab):
+    """The backward (or with --forward the forward) over packed sequences; one JSON line."""
+    dev = torch.device("cuda:0")
+    inp = synth.make_varlen_inputs(vw)
+    q, k, v, do, cu = (inp[n].to(dev) for n in ("q", "k", "v", "dout", "cu"))
+    cul = inp["cu"].tolist()
+    lens = np.diff(cul)
+    mx = inp["max_seqlen"]
+    o = torch.empty_like(q)
+    lse = torch.full((1, vw.Hq, vw.T), -math.inf, dtype=torch.float32, device=dev)
+    for a_, b_ in zip(cul[:-1], cul[1:]):  # input preparation, not timed: fp32 torch forward per sequence
+        if b_ > a_:
+            oo, ll = gpu_forward_inputs(q[:, a_:b_].contiguous(), k[:, a_:b_].contiguous(), v[:, a_:b_].contiguous(), vw)
+            o[:, a_:b_], lse[:, :, a_:b_] = oo, ll
+    stream = torch.cuda.current_stream()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    a = ab.make_args(q, k, v, o, do, lse, dq, dk, dv, scale=vw.scale, causal=vw.causal, window=vw.window,
+                     cu_seqlens=cu, max_seqlen=mx)
+    need = ab.attn_bwd_workspace_size(a)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), need
+    o2, lse2 = torch.empty_like(q), torch.empty_like(lse)
+
+    def call():
+        if args.forward:
+            ab.attn_fwd_varlen(q, k, v, o2, lse2, cu, mx, vw.scale, causal=vw.causal, window=vw.window, stream=stream)
+        else:
+            ab.attn_bwd_ex(a)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    import ctypes
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for row in ev:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    ev_arrays = [(ctypes.c_void_p * 4)(*[e.cuda_event for e in row]) for row in ev]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        if args.forward:
+            ev[s_][0].record(stream)
+            call()
+            ev[s_][1].record(stream)
+        else:
+            a.events = ctypes.cast(ev_arrays[s_], ctypes.c_void_p)
+            call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    a.events = None
+    ms_per_step = wall * 1e3 / args.steps
+    npairs = varlen_pairs(vw, lens)
+    fwd_flops = npairs * 4 * vw.D
+    if args.forward:
+        per = {"fwd": [row[0].elapsed_time(row[1]) * 1e3 for row in ev]}
+        flops, kname, kflops = fwd_flops, "dense_fwd", fwd_flops
+    else:
+        per = {"dq": [row[0].elapsed_time(row[1]) * 1e3 for row in ev],
+               "dkdv": [row[1].elapsed_time(row[2]) * 1e3 for row in ev]}
+        flops, kname, kflops = 2.5 * fwd_flops, "dense_dkdv", npairs * 8 * vw.D
+    kus = statistics.fmean(per["fwd" if args.forward else "dkdv"])
+    ktf = kflops / (kus * 1e-6) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    what = "attn-fwd" if args.forward else "attn-bwd"
+    result = {
+        "metric": what + " TFLOP/s (causal-adjusted) + % of MI355X fp16/bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": vw.dtype,
+        "data": "synthetic: seeded unequal lengths, N(0,1) q,k,v,dO from a seeded PCG64 generator; "
+                "O and lse from an fp32 forward per sequence",
+        "config": {"workload": vw.name + (" (forward)" if args.forward else ""), "T": vw.T, "nseq": vw.nseq,
+                   "lens": [int(x) for x in lens], "Hq": vw.Hq, "Hkv": vw.Hkv, "D": vw.D, "causal": vw.causal,
+                   "window": vw.window, "metric_flops": flops, "pairs": npairs},
+        "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(ktf, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ktf / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": kflops},
+        "kernels_us_median": {n_: round(statistics.median(x), 2) for n_, x in per.items()},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workload", default=synth.HEADLINE,
+                    choices=sorted(synth.WORKLOADS) + sorted(synth.VARLEN_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cold-iters", type=int, default=10)
@@ -296,6 +395,9 @@ def main():
 
     import attention_backward_amd as ab
 
+    if args.workload in synth.VARLEN_WORKLOADS:
+        bench_varlen(args, synth.VARLEN_WORKLOADS[args.workload], ab)
+        return
     w = synth.WORKLOADS[args.workload]
     shared = bool(args.kv_shared)
     if shared and not w.topk:

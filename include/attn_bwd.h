@@ -96,6 +96,22 @@ typedef struct {
                                        V, v and dv must be NULL, and dk receives dKV = dK + [dV, 0],
                                        the gradient with respect to that one tensor.  Requires
                                        topk_idx and Dv <= Dqk.                                   */
+  const int32_t *cu_seqlens;        /* NULL, or packed variable-length sequences on the dense
+                                       path (flash-linear-attention issue #8: packed varlen with
+                                       per-sequence BOS/EOS offsets): a 4-byte aligned device
+                                       array of nseq + 1 non-decreasing token offsets, 0 first and
+                                       Sq last.  Then B = 1, Sq = Skv = T (the packed length),
+                                       every tensor is the batch-of-one layout above (q [1,T,Hq,Dqk],
+                                       lse [1,Hq,T], ...), and sequence s is tokens
+                                       [cu_seqlens[s], cu_seqlens[s+1]): each is its own attention
+                                       problem, the masks taken within it (off = 0).  Offsets are
+                                       clamped into [0, T] on the device, so a bad table cannot
+                                       move an access out of the buffers, but tokens outside
+                                       [0, cu_seqlens[nseq]) and past max_seqlen of a longer
+                                       sequence are then left unwritten.                        */
+  int64_t nseq;                     /* packed: number of sequences (>= 1); else 0              */
+  int64_t max_seqlen;               /* packed: a bound on every sequence length, 1..T (sizes the
+                                       grid; a longer sequence is cut there); else 0            */
 } attn_bwd_args;
 
 /* Bytes of workspace the call needs for these sizes (0 if the arguments are invalid), as
@@ -141,6 +157,14 @@ int attn_bwd_delta(const void *o, const void *dout, float *delta, int64_t B, int
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t Sq, int64_t Skv,
              int64_t Hq, int64_t Hkv, int64_t D, float scale, int32_t causal, int32_t window, int32_t dtype,
              void *stream);
+
+/* attn_fwd over packed variable-length sequences: q, o [1,T,Hq,D], k, v [1,T,Hkv,D], lse [1,Hq,T],
+ * and cu_seqlens, nseq and max_seqlen as in attn_bwd_args (sequence s is tokens
+ * [cu_seqlens[s], cu_seqlens[s+1]), each its own attention problem).  Validation as attn_fwd,
+ * plus ATTN_E_INVAL for a null or misaligned cu_seqlens, nseq < 1, or max_seqlen outside 1..T. */
+int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse, const int32_t *cu_seqlens,
+                    int64_t nseq, int64_t max_seqlen, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                    int32_t causal, int32_t window, int32_t dtype, void *stream);
 
 /* Static description of a status code (never NULL).  For ATTN_E_HIP the string includes the
  * HIP error text of the last failure on the calling thread. */

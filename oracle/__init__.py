@@ -17,6 +17,8 @@ Parity status of each entry point (what pins it is in tests/test_oracle_pins.py)
                         brute-force dense numpy, dS row sums, dV = P^T dO, closed forms
   bwd_dq_rows   pinned: equals the matching rows of bwd (which is pinned)
   bwd_dkv_rows  pinned: equals the matching rows of bwd
+  fwd_varlen,   pinned: brute force over the block-diagonal packed mask, equal lengths equal to
+  bwd_varlen            the dense batch, a sequence's outputs blind to the other sequences
 """
 from __future__ import annotations
 
@@ -165,3 +167,35 @@ def bwd_dkv_rows(q, k, v, o, dout, lse, scale, rows, causal=True, window=0, idx=
     if rc:
         raise ValueError(f"oracle_bwd_dkv_rows failed (rc={rc})")
     return dk, dv
+
+
+def _segments(cu):
+    cu = np.asarray(cu.detach().cpu() if hasattr(cu, "detach") else cu, dtype=np.int64).reshape(-1)
+    return [(int(cu[i]), int(cu[i + 1])) for i in range(cu.size - 1)]
+
+
+def fwd_varlen(q, k, v, cu, scale, causal=True, window=0):
+    """Packed sequences (flash-linear-attention issue #8, packed varlen): q [1,T,Hq,Dqk],
+    k [1,T,Hkv,Dqk], v [1,T,Hkv,Dv] and token offsets cu [nseq + 1]; tokens [cu[s], cu[s+1]) form
+    sequence s, its own attention problem with the masks taken inside it.  Returns
+    o [1,T,Hq,Dv] and lse [1,Hq,T] in f64 (tokens in no sequence: o = 0, lse = -inf)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, Hq, Dv = q.shape[1], q.shape[2], v.shape[3]
+    o = np.zeros((1, T, Hq, Dv))
+    lse = np.full((1, Hq, T), -np.inf)
+    for a, b in _segments(cu):
+        if b > a:
+            o[:, a:b], lse[:, :, a:b] = fwd(q[:, a:b], k[:, a:b], v[:, a:b], scale, causal, window)
+    return o, lse
+
+
+def bwd_varlen(q, k, v, o, dout, lse, cu, scale, causal=True, window=0):
+    """The backward of fwd_varlen's problem: each sequence's slice through bwd.  Returns dq, dk,
+    dv in the packed layout (tokens in no sequence: 0)."""
+    q, k, v, o, dout, lse = (_f64(x) for x in (q, k, v, o, dout, lse))
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for a, b in _segments(cu):
+        if b > a:
+            dq[:, a:b], dk[:, a:b], dv[:, a:b] = bwd(q[:, a:b], k[:, a:b], v[:, a:b], o[:, a:b], dout[:, a:b],
+                                                     lse[:, :, a:b], scale, causal, window)
+    return dq, dk, dv

@@ -32,7 +32,24 @@ def multiplicity(Sq, Skv, causal, window, idx_row=None):
     return M
 
 
-def forward(q, k, v, scale, causal, window, idx=None):
+def multiplicity_packed(cu, causal, window):
+    """M [T, T] for packed sequences (batch of one): key j counts for query i iff both lie in
+    the same sequence [cu[s], cu[s+1]) and the masks hold for their positions inside it."""
+    cu = np.asarray(cu, dtype=np.int64)
+    T = int(cu[-1])
+    t = np.arange(T)
+    seq = np.searchsorted(cu, t, side="right") - 1
+    pos = t - cu[seq]
+    i, j = pos[:, None], pos[None, :]
+    m = seq[:, None] == seq[None, :]
+    if causal:
+        m &= j <= i
+    if window > 0:
+        m &= j > i - window
+    return m.astype(np.float64)
+
+
+def forward(q, k, v, scale, causal, window, idx=None, M_all=None):
     B, Sq, Hq, _ = q.shape
     Skv, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
     G = Hq // Hkv
@@ -41,7 +58,8 @@ def forward(q, k, v, scale, causal, window, idx=None):
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            M = multiplicity(Sq, Skv, causal, window, None if idx is None else idx[b, :, g, :])
+            M = M_all if M_all is not None else multiplicity(Sq, Skv, causal, window,
+                                                             None if idx is None else idx[b, :, g, :])
             s = q[b, :, h, :] @ k[b, :, g, :].T * scale * LOG2E
             has = M.sum(1) > 0
             smax = np.where(M > 0, s, -np.inf).max(1, initial=-np.inf)
@@ -53,7 +71,7 @@ def forward(q, k, v, scale, causal, window, idx=None):
     return o, lse
 
 
-def backward(q, k, v, o, dout, lse, scale, causal, window, idx=None, return_p=False):
+def backward(q, k, v, o, dout, lse, scale, causal, window, idx=None, return_p=False, M_all=None):
     B, Sq, Hq, _ = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
     G = Hq // Hkv
@@ -64,7 +82,8 @@ def backward(q, k, v, o, dout, lse, scale, causal, window, idx=None, return_p=Fa
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            M = multiplicity(Sq, Skv, causal, window, None if idx is None else idx[b, :, g, :])
+            M = M_all if M_all is not None else multiplicity(Sq, Skv, causal, window,
+                                                             None if idx is None else idx[b, :, g, :])
             l = lse[b, h, :]
             live = np.isfinite(l) | (l > 0)
             s = q[b, :, h, :] @ k[b, :, g, :].T

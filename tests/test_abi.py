@@ -26,6 +26,9 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert getattr(lib, n) is not None
 
 
+PACKED = dict(cu_seqlens=0x100000, nseq=3, max_seqlen=2000, B=1, Sq=4096, Skv=4096)
+
+
 def valid_args(**kw):
     a = ab.attn_bwd_args()
     fake = 0x100000  # aligned, never dereferenced: every case below fails validation first
@@ -87,6 +90,18 @@ def test_workspace_size():
               workspace_bytes=16), -3),
         (dict(workspace=0x100080, workspace_bytes=1 << 30), -1),  # workspace not 256-byte aligned
         (dict(workspace=0, workspace_bytes=64), -1),
+        # packed sequences: a batch of one on the dense path
+        (dict(PACKED, B=2), -1),
+        (dict(PACKED, Skv=4000), -1),
+        (dict(PACKED, topk_idx=0x100000, topk=8, Dqk=576, Dv=512), -1),
+        (dict(PACKED, nseq=0), -1),
+        (dict(PACKED, max_seqlen=0), -1),
+        (dict(PACKED, max_seqlen=4097), -1),                  # longer than the packed length
+        (dict(PACKED, cu_seqlens=0x100002), -1),                # misaligned offsets
+        (dict(nseq=3), -1),                                     # sequence sizes without offsets
+        (dict(max_seqlen=100), -1),
+        (dict(PACKED, nseq=1 << 20, max_seqlen=4096), -2),      # grid too large
+        (dict(PACKED, workspace=0x100000, workspace_bytes=16), -3),  # valid up to the workspace
     ],
 )
 def test_validation_statuses(kw, status):
@@ -134,6 +149,30 @@ def test_forward_entry_point_validates(kw, status):
     rc = ab.load().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Sq"], a["Skv"], a["Hq"], a["Hkv"],
                             a["D"], a["scale"], a["causal"], a["window"], a["dtype"], None)
     assert rc == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), -1),
+    (dict(cu=0x100002), -1),
+    (dict(nseq=0), -1),
+    (dict(max_seqlen=0), -1),
+    (dict(max_seqlen=129), -1),     # longer than the packed length
+    (dict(causal=0, window=8), -1),
+    (dict(D=96), -2),
+    (dict(nseq=1 << 20, T=4096, max_seqlen=4096), -2),  # grid too large
+])
+def test_forward_varlen_entry_point_validates(kw, status):
+    a = dict(q=0x100000, k=0x100000, v=0x100000, o=0x100000, lse=0x100000, cu=0x100000, nseq=2, max_seqlen=100,
+             T=128, Hq=4, Hkv=2, D=128, scale=0.088, causal=1, window=0, dtype=0)
+    a.update(kw)
+    rc = ab.load().attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["nseq"], a["max_seqlen"],
+                                   a["T"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["window"],
+                                   a["dtype"], None)
+    assert rc == status
+
+
+def test_packed_workspace_is_the_batch_of_one():
+    assert ab.attn_bwd_workspace_size(valid_args(**PACKED)) == 2 * (32 * 4096 * 4)
 
 
 def test_binding_refuses_cpu_tensors():

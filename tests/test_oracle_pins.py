@@ -356,3 +356,65 @@ def test_lse_minus_inf_row_contributes_nothing():
     ref = bf.backward(q, k, v, o, do, lse2, 0.5, True, 0)
     for a, b in zip((dq, dk, dv), ref):
         np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+VARLEN = [
+    # lengths, Hq, Hkv, D, causal, window
+    ((5, 1, 0, 7, 3), 4, 2, 4, True, 0),
+    ((6, 2, 9), 2, 1, 6, True, 3),
+    ((4, 4, 8), 2, 2, 4, False, 0),
+]
+
+
+@pytest.mark.parametrize("c", VARLEN)
+def test_varlen_matches_bruteforce_packed_mask(c):
+    """Packed sequences against a brute force over one [T, T] block-diagonal mask."""
+    lens, Hq, Hkv, D, causal, window = c
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q, k, v, do = rnd(41, 1, T, T, Hq, Hkv, D, D)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = oracle.fwd_varlen(q, k, v, cu, scale, causal, window)
+    M = bf.multiplicity_packed(cu, causal, window)
+    bo, bl = bf.forward(q, k, v, scale, causal, window, M_all=M)
+    np.testing.assert_allclose(o, bo, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(np.isinf(lse), np.isinf(bl))
+    np.testing.assert_allclose(lse[np.isfinite(lse)], bl[np.isfinite(bl)], rtol=1e-12, atol=1e-12)
+    got = oracle.bwd_varlen(q, k, v, o, do, lse, cu, scale, causal, window)
+    ref = bf.backward(q, k, v, o, do, lse, scale, causal, window, M_all=M)
+    for x, y in zip(got, ref):
+        np.testing.assert_allclose(x, y, rtol=1e-10, atol=1e-12)
+
+
+def test_varlen_equal_lengths_is_the_dense_batch():
+    B, L, Hq, Hkv, D = 3, 7, 4, 2, 4
+    q, k, v, do = rnd(43, B, L, L, Hq, Hkv, D, D)
+    cu = np.arange(B + 1) * L
+    pk = lambda a: a.reshape(1, B * L, *a.shape[2:])  # noqa: E731  [B,L,...] -> [1,B*L,...]
+    o, lse = oracle.fwd(q, k, v, 0.5, True, 3)
+    po, pl = oracle.fwd_varlen(pk(q), pk(k), pk(v), cu, 0.5, True, 3)
+    np.testing.assert_array_equal(po, pk(o))
+    np.testing.assert_array_equal(pl, lse.transpose(1, 0, 2).reshape(1, Hq, B * L))
+    ref = oracle.bwd(q, k, v, o, do, lse, 0.5, True, 3)
+    got = oracle.bwd_varlen(pk(q), pk(k), pk(v), po, pk(do), pl, cu, 0.5, True, 3)
+    for x, y in zip(got, ref):
+        np.testing.assert_array_equal(x, pk(y))
+
+
+def test_varlen_sequences_are_independent():
+    lens = (4, 6, 5)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, do = rnd(47, 1, 15, 15, 2, 1, 4, 4)
+    o, lse = oracle.fwd_varlen(q, k, v, cu, 0.5, True, 0)
+    a = oracle.bwd_varlen(q, k, v, o, do, lse, cu, 0.5, True, 0)
+    q2, k2, v2, do2 = q.copy(), k.copy(), v.copy(), do.copy()
+    for t in (q2, k2, v2, do2):
+        t[:, 4:10] += 1.0  # every token of the middle sequence
+    o2, lse2 = oracle.fwd_varlen(q2, k2, v2, cu, 0.5, True, 0)
+    b = oracle.bwd_varlen(q2, k2, v2, o2, do2, lse2, cu, 0.5, True, 0)
+    keep = np.r_[0:4, 10:15]
+    np.testing.assert_array_equal(o[:, keep], o2[:, keep])
+    np.testing.assert_array_equal(lse[:, :, keep], lse2[:, :, keep])
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x[:, keep], y[:, keep])
+        assert not np.array_equal(x[:, 4:10], y[:, 4:10])
