@@ -26,6 +26,10 @@
 
 namespace attn {
 
+#ifndef ATTN_FWD_PF
+#define ATTN_FWD_PF 3  // LDS operand reads issued ahead of their products
+#endif
+
 template <int D, int BK>
 struct FwdCfg {
   static constexpr int NW = 8;             // waves per workgroup
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(512, 1) void dense_fwd_kernel(const FwdParams p) {
         // k-steps ahead through a ring of registers.
         f16v s = f16v{};
         mfma_prio_hi();
-        ring_pipeline<C::KK, 3>([&](int kk) { return lds_rd16_at(abk[kk] + kb * 64 * D); },
+        ring_pipeline<C::KK, ATTN_FWD_PF>([&](int kk) { return lds_rd16_at(abk[kk] + kb * 64 * D); },
                                 [&](int kk, s8v kr) { s = TT::mfma(kr, qf[kk], s); });
         mfma_prio_lo();
         // Online softmax; register r is key k0 + 32 kb + 8 (r/4) + 4 hi + r%4.  P^T is packed as
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(512, 1) void dense_fwd_kernel(const FwdParams p) {
 #pragma unroll
             for (int half = 0; half < 2; half++)
               ab[dn][half] = lds_base_add(lds_addr(kv_s[buf][1]), tr_lane[dn][half]);
-          ring_pipeline<2 * C::ND, 3>(
+          ring_pipeline<2 * C::ND, ATTN_FWD_PF>(
               [&](int n) {
                 const int kst = 2 * kb + n / C::ND, dn = n % C::ND;
                 return cat8(lds_tr4_at(ab[dn][0] + kst * 32 * D), lds_tr4_at(ab[dn][1] + kst * 32 * D));
@@ -250,9 +254,17 @@ static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t st) {
   return hipGetLastError();
 }
 
+#ifndef ATTN_FWD128_BK
+#define ATTN_FWD128_BK 64
+#endif
+#ifndef ATTN_FWD64_BK
+#define ATTN_FWD64_BK 64
+#endif
+
 hipError_t launch_dense_fwd(const FwdParams &p, int D, bool bf16, hipStream_t st) {
-  if (D == 128) return bf16 ? launch_fwd_t<BF16, 128, 64>(p, st) : launch_fwd_t<F16, 128, 64>(p, st);
-  if (D == 64) return bf16 ? launch_fwd_t<BF16, 64, 64>(p, st) : launch_fwd_t<F16, 64, 64>(p, st);
+  constexpr int B128 = ATTN_FWD128_BK, B64 = ATTN_FWD64_BK;
+  if (D == 128) return bf16 ? launch_fwd_t<BF16, 128, B128>(p, st) : launch_fwd_t<F16, 128, B128>(p, st);
+  if (D == 64) return bf16 ? launch_fwd_t<BF16, 64, B64>(p, st) : launch_fwd_t<F16, 64, B64>(p, st);
   return hipErrorInvalidValue;
 }
 
