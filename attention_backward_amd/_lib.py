@@ -114,7 +114,11 @@ def make_args(q, k, v, o, dout, lse, dq, dk, dv, *, scale, causal=True, window=0
     kv_shared: the shared-latent form of the top-k path; v and dv are None, V is the first Dv
     columns of k and dk receives dK + [dV, 0].
     cu_seqlens: packed sequences (int32 [nseq + 1] on the GPU; tensors [1, T, H, D]); max_seqlen,
-    a host int bounding every length, is then required."""
+    a host int bounding every length, is then required.
+
+    The struct holds raw device pointers, not the tensors: every tensor passed here must stay
+    referenced until the work enqueued with it has run (a temporary such as `o.cuda()` passed
+    inline is freed on return, and torch may hand its memory to the next allocation)."""
     if q.dtype not in _DT:
         raise TypeError(f"unsupported dtype {q.dtype}")
     if kv_shared and (v is not None or dv is not None):
