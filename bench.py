@@ -42,6 +42,9 @@ PROFILED_TRAFFIC = {
     ("dense_dkdv", "mha_causal_b2_s2048_h32_d128_fp16"): dict(
         fetch_kib=112138.8, write_kib=65536.0, fetch_scale=2.000, write_scale=1.000,
         files=("dense_dkdv.hip", "common.h"), sha="b1068c31a18d0977"),
+    ("dense_fwd", "mha_causal_b2_s2048_h32_d128_fp16"): dict(
+        fetch_kib=78207.4, write_kib=33280.0, fetch_scale=2.000, write_scale=1.000,
+        files=("dense_fwd.hip", "common.h", "kernels.h"), sha="355ab6b850a52bf2"),
     ("sparse_dkdv", "sparse_mla_b1_sq4096_skv8192_h64_dqk576_dv512_top2048_bf16"): dict(
         fetch_kib=7479495.5, write_kib=217600.0, fetch_scale=2.000, write_scale=1.000,
         files=("sparse_dkdv.hip", "common.h"), sha="552775905fa59087"),
@@ -198,6 +201,19 @@ def cpu_baseline_topk(w, inp_cpu, target_s, threads):
             "seconds": dt}
 
 
+def calib_copy(args, dev):
+    """After timing: one fp16 -> f32 device copy reading --calib-copy-mib MiB, a known-size kernel
+    against which profiler byte counters are scaled (a conversion, so it runs an elementwise
+    kernel; a same-dtype copy would be a DMA transfer)."""
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 19, dtype=torch.float16, device=dev)
+        dst = torch.empty(src.shape, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+
 def bench_forward(args, w, ab, with_bwd=False):
     """The forward alone (or forward + backward per step): K back-to-back calls on resident q, k, v
     (and dO); one JSON line.  The roofline is the forward kernel's, from events around it."""
@@ -236,6 +252,7 @@ def bench_forward(args, w, ab, with_bwd=False):
     wall = time.perf_counter() - t0
     per = [row[0].elapsed_time(row[1]) * 1e3 for row in ev]
     per_b = [row[1].elapsed_time(row[2]) * 1e3 for row in ev]
+    calib_copy(args, dev)
     ms_per_step = wall * 1e3 / args.steps
     npairs = pairs(w)
     fwd_flops = npairs * (2 * w.Dqk + 2 * w.Dv)  # S = Q K^T and O = P V over the unmasked pairs
@@ -261,7 +278,8 @@ def bench_forward(args, w, ab, with_bwd=False):
                    "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal, "window": w.window, "metric_flops": flops,
                    "pairs": npairs},
         "roofline": {"kernel": "dense_fwd", "bound": "mfma", "achieved": round(ktf, 2), "peak": PEAK_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ktf / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(ktf / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": profiled_traffic("dense_fwd", w.name), "traffic_unit": "bytes per launch",
                      "algorithmic_flops_per_launch": fwd_flops},
         "kernels_us_median": {"fwd": round(statistics.median(per), 2)} |
                              ({"bwd_call": round(statistics.median(per_b), 2)} if with_bwd else {}),
@@ -471,15 +489,7 @@ def main():
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1) * 1e3)
     del flush
-    if args.calib_copy_mib:
-        # fp16 -> f32 conversion copy: reads 2 bytes and writes 4 bytes per element, so it runs a
-        # plain elementwise kernel (a same-dtype copy would be a DMA transfer, not a kernel).
-        src = torch.ones(args.calib_copy_mib << 19, dtype=torch.float16, device=dev)
-        dst = torch.empty(src.shape, dtype=torch.float32, device=dev)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calib_copy(args, dev)
 
     npairs = pairs(w)
     flops = 2.5 * npairs * (2 * w.Dqk + 2 * w.Dv)
