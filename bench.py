@@ -148,32 +148,39 @@ def gpu_forward_inputs(q, k, v, w, idx=None):
 
 def cpu_baseline(w, inp_cpu, target_s):
     """The f64 CPU oracle, as it stands, on a bounded sample of the workload: the full backward of
-    the first n heads of batch 0 (n chosen so the run takes about target_s seconds)."""
+    the first nb batches and their first nh heads (nh grown first, then nb, so that the run takes
+    about target_s seconds; the whole workload when it fits)."""
     import oracle  # the oracle is test infrastructure; this leg only times it
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
 
-    def run(nh):
+    def run(nb, nh):
         G = w.G
         nkv = max(1, nh // G)
         nh = nkv * G
-        sl = lambda t, n: t[:1, :, :n].contiguous()  # noqa: E731
+        sl = lambda t, n: t[:nb, :, :n].contiguous()  # noqa: E731
         args = (sl(inp_cpu["q"], nh), sl(inp_cpu["k"], nkv), sl(inp_cpu["v"], nkv), sl(inp_cpu["o"], nh),
-                sl(inp_cpu["dout"], nh), inp_cpu["lse"][:1, :nh].contiguous())
+                sl(inp_cpu["dout"], nh), inp_cpu["lse"][:nb, :nh].contiguous())
         t0 = time.perf_counter()
         oracle.bwd(*args, w.scale, w.causal, w.window)
         return time.perf_counter() - t0, nh
 
     if w.topk:
         return cpu_baseline_topk(w, inp_cpu, target_s, threads)
-    dt1, nh1 = run(w.G)
+    dt1, nh1 = run(1, w.G)
     nh = min(w.Hq, max(nh1, int(nh1 * target_s / max(dt1, 1e-3))))
-    dt, nh = run(nh) if nh > nh1 else (dt1, nh1)
-    sample = w.with_(B=1, Hq=nh, Hkv=max(1, nh // w.G))
+    dt, nh = run(1, nh) if nh > nh1 else (dt1, nh1)
+    nb = 1
+    if nh == w.Hq and w.B > 1 and dt < target_s / 2:
+        nb = min(w.B, max(1, int(target_s / max(dt, 1e-3))))
+        if nb > 1:
+            dt, nh = run(nb, nh)
+    sample = w.with_(B=nb, Hq=nh, Hkv=max(1, nh // w.G))
     flops = 2.5 * pairs(sample) * (2 * w.Dqk + 2 * w.Dv)
+    what = "the whole workload" if (nb, nh) == (w.B, w.Hq) else \
+        f"batches 0..{nb - 1}, query heads 0..{nh - 1} of {w.Hq} ({nb * nh}/{w.B * w.Hq} of the workload's heads)"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"full f64 backward of batch 0, query heads 0..{nh - 1} of {w.Hq} ({nh}/{w.B * w.Hq} of the "
-                      f"workload's heads), {dt:.1f} s", "seconds": dt}
+            "sample": f"full f64 backward of {what}, {dt:.1f} s", "seconds": dt}
 
 
 def cpu_baseline_topk(w, inp_cpu, target_s, threads):
@@ -199,6 +206,21 @@ def cpu_baseline_topk(w, inp_cpu, target_s, threads):
             "sample": f"full f64 backward of batch 0, the last {n} of {w.Sq} query rows with all {w.Hq} heads and "
                       f"their top-{w.topk} lists ({n}/{w.B * w.Sq} of the workload's rows), {dt:.1f} s",
             "seconds": dt}
+
+
+def gpu_state():
+    """Temperature and clock readings of the GPU from rocm-smi, run as a child process (None where
+    the tool or its output is unavailable): a throttled clock compresses differences."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showtemp", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+        card = next(v for k, v in sorted(d.items()) if k.lower().startswith("card"))
+        return {k: v for k, v in card.items() if "emperature" in k or "clock" in k.lower()}
+    except Exception:  # noqa: BLE001 -- a missing reading is reported as null
+        return None
 
 
 def calib_copy(args, dev):
@@ -443,6 +465,7 @@ def main():
     a.workspace, a.workspace_bytes = ws.data_ptr(), need
     stream = torch.cuda.current_stream()
 
+    state_before = gpu_state()
     for _ in range(args.warmup):
         ab.attn_bwd_ex(a)
     torch.cuda.synchronize()
@@ -464,6 +487,7 @@ def main():
         ab.attn_bwd_ex(a)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    state_after = gpu_state()
     a.events = None
     # The library records its events between its phases: dense = dQ kernel (with the preprocess
     # in its prologue) | dK/dV kernel | (nothing); top-k = preprocess, zero-fill, key counts and
@@ -550,8 +574,12 @@ def main():
         "kernels_us_median": {kname: round(v_, 2) for kname, v_ in med.items()},
         "kernels": kernels,
         "cold_call_us": None if not cold else {
-            "median": round(statistics.median(cold), 2), "min": round(min(cold), 2), "max": round(max(cold), 2),
-            "n": len(cold), "tflops_at_median": round(flops / (statistics.median(cold) * 1e-6) / 1e12, 1)},
+            "median": round(statistics.median(cold), 2), "mean": round(statistics.fmean(cold), 2),
+            "std": round(statistics.pstdev(cold), 2), "min": round(min(cold), 2),
+            "p10": round(float(np.percentile(cold, 10)), 2), "p90": round(float(np.percentile(cold, 90)), 2),
+            "max": round(max(cold), 2), "n": len(cold),
+            "tflops_at_median": round(flops / (statistics.median(cold) * 1e-6) / 1e12, 1)},
+        "gpu_state": {"before": state_before, "after_timed_steps": state_after},
     }
     if not args.no_cpu_baseline:
         inp_cpu = {n: inp[n] for n in ("q", "k", "v", "dout", "idx")}
