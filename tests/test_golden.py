@@ -5,7 +5,10 @@
   pages' equations fix (the first query row of a causal call attends only key 0, so its dS and dq
   are exactly 0; dv columns sum to the dout of rows that attend some key).
 - On the GPU: the HIP path, given the stored inputs, O and lse, matches the stored dq/dk/dv within
-  |gpu - ref| <= 5e-3 + 1e-2 |ref| at shapes smaller than one tile of any kernel.
+  |gpu - ref| <= 5e-3 + 1e-2 |ref| at shapes smaller than one tile of any kernel; and the HIP
+  forward, given the stored inputs, reproduces the stored O (the same tolerance; O is stored in the
+  element type, so the bound also covers one rounding of it) and lse (|gpu - ref| <= 1e-3, base 2;
+  lse is stored as f32).
 """
 import json
 import os
@@ -92,3 +95,22 @@ def test_hip_path_matches_stored_values(name):
     torch.cuda.synchronize()
     for n, got in (("dq", dq), ("dk", dk), ("dv", dv)):
         check_close(n, got.cpu().double().numpy().reshape(-1), np.asarray(rec[n]))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", NAMES)
+def test_hip_forward_matches_stored_values(name):
+    import attention_backward_amd as ab
+    from tests.helpers import check_close, log, poisoned_like
+
+    rec = load(name)
+    w = rec["workload"]
+    log(f"golden forward case {name}: {w}")
+    g = {n: v.cuda() for n, v in tensors(rec).items()}
+    o, lse = poisoned_like(g["o"]), poisoned_like(g["lse"])
+    ab.attn_fwd(g["q"], g["k"], g["v"], o, lse, rec["scale"], causal=w["causal"], window=w["window"])
+    torch.cuda.synchronize()
+    check_close("o", o.cpu().double().numpy().reshape(-1), np.asarray(rec["o"]))
+    err = np.abs(lse.cpu().double().numpy().reshape(-1) - np.asarray(rec["lse"]))
+    log(f"  lse: max|err| {err.max():.3e}")
+    assert np.all(err <= 1e-3)
