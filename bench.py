@@ -40,8 +40,8 @@ METRIC = "attn-bwd TFLOP/s (causal-adjusted) + % of MI355X fp16/bf16 MFMA peak"
 # files at the time: once the sources change, the figure no longer applies and is reported as null.
 PROFILED_TRAFFIC = {
     ("dense_dkdv", "mha_causal_b2_s2048_h32_d128_fp16"): dict(
-        fetch_kib=112138.8, write_kib=65536.0, fetch_scale=2.000, write_scale=1.000,
-        files=("dense_dkdv.hip", "common.h"), sha="b1068c31a18d0977"),
+        fetch_kib=111000.5, write_kib=65536.0, fetch_scale=2.000, write_scale=1.000,
+        files=("dense_dkdv.hip", "common.h"), sha="9f901def41964a17"),
     ("dense_fwd", "mha_causal_b2_s2048_h32_d128_fp16"): dict(
         fetch_kib=78207.4, write_kib=33280.0, fetch_scale=2.000, write_scale=1.000,
         files=("dense_fwd.hip", "common.h", "kernels.h"), sha="355ab6b850a52bf2"),
@@ -209,16 +209,25 @@ def cpu_baseline_topk(w, inp_cpu, target_s, threads):
 
 
 def gpu_state():
-    """Temperature and clock readings of the GPU from rocm-smi, run as a child process (None where
-    the tool or its output is unavailable): a throttled clock compresses differences."""
-    import subprocess
+    """Temperature and clock levels of the benchmarked GPU, read from its sysfs files (plain file
+    reads, no child process; None where they are unavailable): a throttled clock compresses
+    differences."""
+    import glob
 
     try:
-        r = subprocess.run(["rocm-smi", "--showtemp", "--showclocks", "--json"], capture_output=True, text=True,
-                           timeout=20)
-        d = json.loads(r.stdout)
-        card = next(v for k, v in sorted(d.items()) if k.lower().startswith("card"))
-        return {k: v for k, v in card.items() if "emperature" in k or "clock" in k.lower()}
+        pr = torch.cuda.get_device_properties(0)
+        bus = "%04x:%02x:%02x" % (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
+        card = next(c for c in sorted(glob.glob("/sys/class/drm/card*/device")) if bus in os.path.realpath(c))
+        out = {}
+        for t in sorted(glob.glob(card + "/hwmon/hwmon*/temp*_input")):
+            lab = t[: -len("_input")] + "_label"
+            name = open(lab).read().strip() if os.path.exists(lab) else os.path.basename(t)
+            out[f"temp_{name}_C"] = int(open(t).read()) / 1000
+        for f in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            if os.path.exists(os.path.join(card, f)):
+                cur = [ln for ln in open(os.path.join(card, f)).read().splitlines() if ln.rstrip().endswith("*")]
+                out[f] = cur[0].split(":", 1)[1].strip(" *") if cur else None
+        return out or None
     except Exception:  # noqa: BLE001 -- a missing reading is reported as null
         return None
 

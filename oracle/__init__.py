@@ -58,6 +58,13 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
+            import sys
+
+            torch = sys.modules.get("torch")
+            if torch is not None and torch.cuda.is_initialized():
+                # No compiler child from a process that has set up the GPU: build beforehand.
+                raise RuntimeError(f"{_LIB_PATH} is missing: build it first (python -c 'import oracle; "
+                                   "oracle.build()') before any GPU work in this process")
             build(force=False)
         lib = ctypes.CDLL(_LIB_PATH)
         p = ctypes.c_void_p
