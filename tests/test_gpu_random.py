@@ -1,5 +1,7 @@
 """Randomised parity sweep: seeded small shapes drawn across every dense option, forward and
-backward through the C ABI against the f64 oracle, plus random packed-length mixes.
+backward through the C ABI against the f64 oracle, plus random packed-length mixes and random
+top-k problems (including corrupted lists: duplicates, padding, out-of-range and non-causal
+entries).
 
 Each case is drawn from its own seed (printed before it runs), so a failure names a shape that
 reproduces.  Sizes stay small enough for the oracle to finish in about a second, but the draws
@@ -19,8 +21,9 @@ from tests.test_gpu_forward import check_lse
 
 pytestmark = pytest.mark.gpu
 
-N_DENSE = 24
-N_PACKED = 8
+N_DENSE = 96
+N_PACKED = 32
+N_TOPK = 12
 
 
 def draw_dense(seed):
@@ -98,5 +101,33 @@ def test_random_packed_forward_and_backward(seed):
     ab.attn_bwd_ex(args)
     torch.cuda.synchronize()
     ref = oracle.bwd_varlen(inp["q"], inp["k"], inp["v"], o_st, inp["dout"], lse32, inp["cu"], w.scale, causal, window)
+    for name, got, r_ in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        check_close(name, got.cpu().double().numpy(), r_)
+
+
+@pytest.mark.parametrize("seed", range(N_TOPK))
+def test_random_topk_backward(seed):
+    r = np.random.default_rng(5000 + seed)
+    Hkv = int(r.choice([1, 2]))
+    G = int(r.choice([1, 8, 16, 32, 40, 64 // Hkv]))
+    Sq, Skv = int(r.integers(1, 120)), int(r.integers(1, 200))
+    w = synth.Workload(f"rand_topk{seed}", int(r.integers(1, 3)), Sq, Skv, Hkv * G, Hkv, 576, 512,
+                       str(r.choice(["fp16", "bf16"])), bool(r.random() < 0.8), 0, int(r.integers(1, 130)),
+                       6000 + seed)
+    log(f"random top-k case {w.name}: B={w.B} Sq={Sq} Skv={Skv} Hq={w.Hq} Hkv={Hkv} topk={w.topk} {w.dtype} "
+        f"causal={w.causal}")
+    inp = synth.make_inputs(w)
+    idx = inp["idx"]
+    if r.random() < 0.5:  # corrupt a tenth of the entries
+        m = torch.from_numpy(r.random(idx.shape) < 0.1)
+        idx = torch.where(m, torch.from_numpy(r.integers(-2, Skv + 3, size=idx.shape).astype(np.int32)), idx)
+    o64, lse64 = oracle.fwd(inp["q"], inp["k"], inp["v"], w.scale, w.causal, 0, idx.numpy())
+    o_st = torch.from_numpy(o64).to(synth.DTYPES[w.dtype])
+    lse32 = torch.from_numpy(lse64).to(torch.float32)
+    g = to_gpu(inp)
+    o_dev, lse_dev, idx_dev = o_st.cuda(), lse32.cuda(), idx.cuda()
+    dq, dk, dv = ab.backward(g["q"], g["k"], g["v"], o_dev, g["dout"], lse_dev, causal=w.causal, topk_idx=idx_dev)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(inp["q"], inp["k"], inp["v"], o_st, inp["dout"], lse32, w.scale, w.causal, 0, idx.numpy())
     for name, got, r_ in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         check_close(name, got.cpu().double().numpy(), r_)
