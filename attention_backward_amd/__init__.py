@@ -3,11 +3,15 @@
 The computation lives in libattn_bwd.so (hand-written HIP kernels for gfx950, C ABI declared
 in include/attn_bwd.h); this package is its ctypes binding plus the seeded input generator.
 
-    from attention_backward_amd import backward
+    from attention_backward_amd import backward, forward
+    o, lse = forward(q, k, v, causal=True)               # dense masks, D in {64, 128}
     dq, dk, dv = backward(q, k, v, o, dout, lse, causal=True)
 
 q [B,Sq,Hq,Dqk], k [B,Skv,Hkv,Dqk], v [B,Skv,Hkv,Dv], o/dout [B,Sq,Hq,Dv] fp16 or bf16 on the
-GPU; lse [B,Hq,Sq] float32, base 2 (natural-log LSE times log2(e)).
+GPU; lse [B,Hq,Sq] float32, base 2 (natural-log LSE times log2(e)).  backward() also takes a
+sliding window (window=), a top-k key list per query (topk_idx=, Dqk 576 / Dv 512); packed
+variable-length sequences go through make_args(..., cu_seqlens=, max_seqlen=) + attn_bwd_ex and
+attn_fwd_varlen.
 """
 from __future__ import annotations
 
