@@ -43,6 +43,10 @@ struct Params {
   float c;                            // scale * log2(e)
   const int32_t *cu;                  // packed sequences: [nseq + 1] token offsets, or null
   int nseq, max_seqlen;               // packed sequences: their number and a bound on each length
+  int hsplit = 1;                     // dense dK/dV: items sharing one key block's query heads
+  float *dk_acc = nullptr;            // hsplit > 1: zeroed f32 [tokens, Hkv, D] the parts add into
+  float *dv_acc = nullptr;
+  int *work = nullptr;                // dense dK/dV work-queue counter (zeroed), or null
 };
 
 // The sequence one workgroup works on.  Dense: batch s of equal-length sequences.  Packed (cu not

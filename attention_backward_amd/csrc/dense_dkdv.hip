@@ -24,6 +24,8 @@
 // tiles entirely outside the mask are never visited; tiles fully inside it skip the mask.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -47,39 +49,57 @@ struct DkdvCfg {
   static_assert(BN <= 64, "lse/delta rows are loaded by one wave instruction each");
 };
 
-template <class TT, int D, int BN>
-__global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
-  using C = DkdvCfg<D, BN>;
-  __shared__ __attribute__((aligned(16))) short q_s[3][BN * D];  // Q of steps t-1, t, t+1
-  __shared__ __attribute__((aligned(16))) short do_s[2][BN * D];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][64];
-  __shared__ __attribute__((aligned(16))) float dl_s[2][64];
 #ifndef ATTN_P_HALF
 #define ATTN_P_HALF 1
 #endif
-  // P crosses from the P role to the dS role through LDS.  fp16: as the element-type operand the
-  // dV product already uses (half the bytes of f32; dS = P (dP - delta) then starts from that
-  // rounding, 2^-12 relative, next to the rounding of dS itself for the dK product; measured
-  // 2.7% faster).  bf16 (8-bit mantissa, hence the hi + lo operands): f32.
-  constexpr bool PH = ATTN_P_HALF && !TT::SPLIT;
-  __shared__ f4v p_s[PH ? 1 : 4][C::MB][4][64];  // f32 P: [key group][query block][reg quarter][lane]
-  __shared__ s8v ph_s[PH ? 4 : 1][C::KS][64];     // element-type P: [key group][k-step][lane]
+
+// LDS of one dK/dV workgroup.  P crosses from the P role to the dS role through it.  fp16: as
+// the element-type operand the dV product already uses (half the bytes of f32; dS = P (dP -
+// delta) then starts from that rounding, 2^-12 relative, next to the rounding of dS itself for
+// the dK product; measured 2.7% faster).  bf16 (8-bit mantissa, hence the hi + lo operands): f32.
+template <class TT, int D, int BN>
+struct DkdvLds {
+  static constexpr bool PH = ATTN_P_HALF && !TT::SPLIT;
+  __attribute__((aligned(16))) short q_s[3][BN * D];  // Q of steps t-1, t, t+1
+  __attribute__((aligned(16))) short do_s[2][BN * D];
+  __attribute__((aligned(16))) float lse_s[2][64];
+  __attribute__((aligned(16))) float dl_s[2][64];
+  f4v p_s[PH ? 1 : 4][BN / 32][4][64];  // f32 P: [key group][query block][reg quarter][lane]
+  s8v ph_s[PH ? 4 : 1][BN / 16][64];    // element-type P: [key group][k-step][lane]
+};
+
+// One work item: key block kb = item / BH of (sequence or batch, KV head, part of the head group).
+// `rotate`: the one-item-per-workgroup launch spreads packed sequences over the XCDs.
+template <class TT, int D, int BN>
+__device__ __forceinline__ void dkdv_item(const Params &p, const int item, const bool rotate, DkdvLds<TT, D, BN> &L) {
+  using C = DkdvCfg<D, BN>;
+  constexpr bool PH = DkdvLds<TT, D, BN>::PH;
+  auto &q_s = L.q_s;
+  auto &do_s = L.do_s;
+  auto &lse_s = L.lse_s;
+  auto &dl_s = L.dl_s;
+  auto &p_s = L.p_s;
+  auto &ph_s = L.ph_s;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int role = w >> 2, kgrp = w & 3;
   const int hi = lane >> 5, lo = lane & 31;
   const int i16 = lane & 15, g16 = lane >> 4;
-  const int BH = (p.cu ? p.nseq : p.B) * p.Hkv;
-  const int kb = blockIdx.x / BH;
+  // hsplit items share a key block: part sp walks query heads [sp * Gs, (sp + 1) * Gs) of the KV
+  // head's group and adds its finished block into f32 accumulators.
+  const int BH = (p.cu ? p.nseq : p.B) * p.Hkv * p.hsplit;
+  const int kb = item / BH;
   // Packed sequences without a window: rotate the (sequence, head) index by the key block.
   // Workgroups go round-robin over the 8 XCDs, so with (sequences x heads) a multiple of 8 every
   // block of one sequence would land on the same few XCDs, and one long sequence would leave the
   // rest idle (measured 3.4x slower).  Under a window, neighbouring key blocks share most of their
   // query rows and the plain order keeps more of them in one L2 (measured 25% faster).
-  const int rot = p.cu && p.window == 0 ? kb : 0;
-  const int bg = (blockIdx.x % BH + rot) % BH;
-  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int rot = rotate && p.cu && p.window == 0 ? kb : 0;
+  const int bgs = (item % BH + rot) % BH;
+  const int bg = bgs / p.hsplit, sp = bgs % p.hsplit;
+  const int Gs = p.G / p.hsplit;
+  const int b = bg / p.Hkv, g = bg % p.Hkv, h0 = g * p.G + sp * Gs;
   const int k0 = kb * C::BM;
   const SeqView sv = seq_view(p.cu, b, p.Sq, p.Skv, p.Hq, p.max_seqlen);
   const int Sq = sv.Sq, Skv = sv.Skv;
@@ -111,13 +131,13 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
   if (p.window > 0) q_hi = min(Sq, k0 + C::BM - 1 - off + p.window);
   const int qb_lo = q_lo / BN;
   const int qb_hi = q_hi > q_lo ? (q_hi + BN - 1) / BN : qb_lo;
-  const int nsteps = (qb_hi - qb_lo) * p.G;
+  const int nsteps = (qb_hi - qb_lo) * Gs;
 
   // Direct global->LDS loads of step t's Q/dO tile (rows past Sq are clamped to the last row;
   // the mask zeroes them) and of its lse/delta rows.
   auto issue = [&](int t, int qbuf, int buf) {
-    const int q0 = (qb_lo + t / p.G) * BN;
-    const int h = g * p.G + t % p.G;
+    const int q0 = (qb_lo + t / Gs) * BN;
+    const int h = h0 + t % Gs;
 #pragma unroll
     for (int u = 0; u < C::WIW; u++) {
       const int slot0 = (w * C::WIW + u) * 64;
@@ -222,7 +242,7 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
       s[mb] = TT::mfma(ring[n % (PF + 1)], kv[kk], s[mb]);
     }
   };
-  auto step_q0 = [&](int t) { return (qb_lo + t / p.G) * BN; };
+  auto step_q0 = [&](int t) { return (qb_lo + t / Gs) * BN; };
   auto step_full = [&](int q0) {
     return (!p.causal || k0 + C::BM - 1 <= q0 + off) && (p.window <= 0 || k0 > q0 + BN - 1 + off - p.window) &&
            (q0 + BN <= Sq) && (k0 + C::BM <= Skv);
@@ -316,8 +336,21 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
   }
 
   // Epilogue: dV (P role) or scale * dK (dS role), cast once, BSHD at the KV head.
-  short *dst = role == 0 ? p.dv : p.dk;
   const float sc = role == 0 ? 1.f : p.scale;
+  if (p.hsplit > 1) {  // one f32 add per element of this part's block (two parts: either order)
+    float *acc_out = role == 0 ? p.dv_acc : p.dk_acc;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int key = kbase + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (key < Skv) {
+        float *row = acc_out + ((sv.k0 + key) * p.Hkv + g) * D + lo;
+#pragma unroll
+        for (int dn = 0; dn < C::ND; dn++) unsafeAtomicAdd(&row[32 * dn], acc[dn][r]);
+      }
+    }
+    return;
+  }
+  short *dst = role == 0 ? p.dv : p.dk;
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     const int key = kbase + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -330,11 +363,44 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
 }
 
 template <class TT, int D, int BN>
+__global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
+  __shared__ DkdvLds<TT, D, BN> L;
+  dkdv_item<TT, D, BN>(p, blockIdx.x, true, L);
+}
+
+// Work-queue form: one workgroup per CU takes items in index order (key blocks longest first)
+// from a counter that starts at zero, so a free CU always gets the next item whatever XCD it is
+// on.  Every workgroup leaves once the counter passes the item count; all its waves see the same
+// item through LDS between two barriers.
+template <class TT, int D, int BN>
+__global__ __launch_bounds__(512, 1) void dense_dkdv_queue_kernel(const Params p, int nitems) {
+  __shared__ DkdvLds<TT, D, BN> L;
+  __shared__ int next;
+  for (;;) {
+    if (threadIdx.x == 0) next = atomicAdd(p.work, 1);
+    __syncthreads();
+    const int u = next;
+    __syncthreads();
+    if (u < 0 || u >= nitems) break;
+    dkdv_item<TT, D, BN>(p, u, false, L);
+  }
+}
+
+template <class TT, int D, int BN>
 static hipError_t launch_dkdv_t(const Params &p, hipStream_t st) {
   const int nkb = ((p.cu ? p.max_seqlen : p.Skv) + DkdvCfg<D, BN>::BM - 1) / DkdvCfg<D, BN>::BM;
-  const int64_t blocks = (int64_t)nkb * (p.cu ? p.nseq : p.B) * p.Hkv;
-  if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL((dense_dkdv_kernel<TT, D, BN>), dim3((unsigned)blocks), dim3(512), 0, st, p);
+  const int64_t items = (int64_t)nkb * (p.cu ? p.nseq : p.B) * p.Hkv * p.hsplit;
+  if (items < 1) return hipSuccess;
+  if (p.work) {
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int grid = (int)std::min<int64_t>(items, std::max(ncu, 1));
+    hipLaunchKernelGGL((dense_dkdv_queue_kernel<TT, D, BN>), dim3(grid), dim3(512), 0, st, p, (int)items);
+  } else {
+    hipLaunchKernelGGL((dense_dkdv_kernel<TT, D, BN>), dim3((unsigned)items), dim3(512), 0, st, p);
+  }
   return hipGetLastError();
 }
 

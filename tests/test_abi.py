@@ -171,8 +171,15 @@ def test_forward_varlen_entry_point_validates(kw, status):
     assert rc == status
 
 
-def test_packed_workspace_is_the_batch_of_one():
-    assert ab.attn_bwd_workspace_size(valid_args(**PACKED)) == 2 * (32 * 4096 * 4)
+def test_packed_workspace():
+    """delta and lse as for the batch of one; without a window, f32 dK/dV accumulators when the
+    head group (here 32 / 8) splits in two halves, then 256 bytes for the dK/dV work-queue
+    counter."""
+    acc = 4096 * 8 * 128 * 4
+    assert ab.attn_bwd_workspace_size(valid_args(**dict(PACKED, Hkv=8))) == 2 * (32 * 4096 * 4) + 2 * acc + 256
+    # a head group of one cannot split: the counter only
+    assert ab.attn_bwd_workspace_size(valid_args(**PACKED)) == 2 * (32 * 4096 * 4) + 256
+    assert ab.attn_bwd_workspace_size(valid_args(**dict(PACKED, window=100))) == 2 * (32 * 4096 * 4)
 
 
 def test_binding_refuses_cpu_tensors():

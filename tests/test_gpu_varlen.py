@@ -86,7 +86,10 @@ def test_varlen_small_full_parity(w):
 
 def test_single_packed_sequence_is_the_dense_batch_of_one():
     """Same kernels, same per-row arithmetic: a packed call holding one sequence gives the bits of
-    the dense call with B = 1."""
+    the dense call with B = 1 for O, lse and dQ.  dK and dV differ in rounding only: the packed
+    call splits each head group into two halves whose f32 sums add into zeroed accumulators, where
+    the dense call sums the whole group in one workgroup.  Both halves add onto zero, in either
+    order the same sum, so repeated packed calls agree bit for bit."""
     w = vw("vl_one", (777,), 4, 2, 128, "fp16", True, 0, 410)
     inp = synth.make_varlen_inputs(w)
     _, _, o_st, lse32 = oracle_o_lse(inp, w)
@@ -98,12 +101,16 @@ def test_single_packed_sequence_is_the_dense_batch_of_one():
     assert torch.equal(o_p.view(torch.int16), o_d.cpu().view(torch.int16))
     assert torch.equal(lse_p.view(torch.int32), lse_d.cpu().view(torch.int32))
     packed = gpu_bwd(inp, o_st, lse32, w)
+    again = gpu_bwd(inp, o_st, lse32, w)
+    for x, y in zip(packed, again):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16)), "two identical packed calls differ"
     g = {n: inp[n].cuda() for n in ("q", "k", "v", "dout")}
     dq, dk, dv = poisoned_like(g["q"]), poisoned_like(g["k"]), poisoned_like(g["v"])
     ab.backward(g["q"], g["k"], g["v"], o_st.cuda(), g["dout"], lse32.cuda(), causal=True, out=(dq, dk, dv))
     torch.cuda.synchronize()
-    for x, y in zip(packed, (dq.cpu(), dk.cpu(), dv.cpu())):
-        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(packed[0].view(torch.int16), dq.cpu().view(torch.int16))
+    for name, x, y in zip(("dk", "dv"), packed[1:], (dk.cpu(), dv.cpu())):
+        check_close(name, x.double().numpy(), y.double().numpy())
 
 
 @pytest.mark.parametrize("name", sorted(synth.VARLEN_WORKLOADS))
