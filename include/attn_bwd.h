@@ -119,9 +119,10 @@ typedef struct {
  *   delta (stored negated) and a sanitised copy of lse, [B,Hq,Sq] f32 each;
  *   top-k only: f32 accumulators dK_acc [B,Skv,Hkv,Dqk] and dV_acc [B,Skv,Hkv,Dv] and the
  *   16-bit key counts;
- *   packed sequences without a window: f32 dK/dV accumulators [T,Hkv,D] each when Hq / Hkv is
- *   even (the two halves of each head group add into them: two adds onto zero, so the result
- *   is still identical between calls), then 256 bytes for the dK/dV work-queue counter.
+ *   without a window, packed sequences, and dense calls with Hq / Hkv >= 8 and even: f32 dK/dV
+ *   accumulators [B*Skv,Hkv,D] each when Hq / Hkv is even (the two halves of each head group
+ *   add into them: two adds onto zero, so the result is still identical between calls), then
+ *   256 bytes for the dK/dV work-queue counter.
  * Never an Hq-shaped dK/dV buffer.  Top-k results: dq is written once per element; dk and dv
  * (or dKV in the shared-latent form) are sums of f32 atomic additions, so their last bits may
  * differ between identical calls.  The shared-latent form needs the same workspace. */

@@ -43,8 +43,13 @@ def valid_args(**kw):
 
 def test_workspace_size():
     assert ab.attn_bwd_workspace_size(valid_args()) == 2 * (2 * 32 * 2048 * 4)
-    # never Hq-shaped dK/dV: GQA needs the same delta-only workspace
-    assert ab.attn_bwd_workspace_size(valid_args(Hkv=4)) == 2 * (2 * 32 * 2048 * 4)
+    # never Hq-shaped dK/dV: a head group of 2 or 4 needs the same delta-only workspace
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=8)) == 2 * (2 * 32 * 2048 * 4)
+    # a head group of 8 or more, no window: the dK/dV work queue, with f32 dK/dV accumulators
+    # at Hkv for its two halves and 256 bytes for the counter
+    acc = 2 * 2048 * 4 * 128 * 4
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=4)) == 2 * (2 * 32 * 2048 * 4) + 2 * acc + 256
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=4, window=64)) == 2 * (2 * 32 * 2048 * 4)
     assert ab.attn_bwd_workspace_size(valid_args(B=1, Sq=3, Hq=2, Hkv=2)) == 512  # 256-byte granularity
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=5)) == 0
     # top-k: delta and lse rows, f32 dK/dV accumulators at Hkv, u16 key counts [B,Hkv,Sq,Skv]
