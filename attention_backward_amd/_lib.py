@@ -51,11 +51,10 @@ _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """Load the library (raises if it has not been built).  ATTN_BWD_LIB may name another build
-    of the same library (e.g. one compiled with different tile parameters) to load instead."""
+    """Load the in-tree library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        path = os.environ.get("ATTN_BWD_LIB") or LIB_PATH
+        path = LIB_PATH
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with `python -m attention_backward_amd.build`")
         lib = ctypes.CDLL(path)

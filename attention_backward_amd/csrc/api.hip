@@ -1,12 +1,15 @@
 // api.hip -- the extern "C" boundary of libattn_bwd.so (declared in include/attn_bwd.h).
 //
-// Validates every argument on the host before anything is enqueued, carves the workspace,
-// and enqueues the kernels on the caller's stream:
-//   dense:  delta (preprocess) -> dK/dV (KV-block owned) -> dQ (query-block owned)
+// Validates every argument on the host before anything is enqueued, carves the caller's
+// workspace, and enqueues the kernels on the caller's stream:
+//   dense:  dQ (query-block owned; its prologue forms delta and the lse copy) -> dK/dV
+//           (KV-block owned, stored once at Hkv); packed calls without a window: dK/dV on a work
+//           queue, with an even head group split in two halves whose f32 slices a landing pass
+//           adds in a fixed order and casts;
 //   top-k:  zero the f32 dK/dV accumulators and the key-count mask, delta, count the keys of
 //           every list -> gathered dQ (query-owned) -> dK/dV (key-owned, weighted by the
 //           counts, added into the accumulators) -> landing (scale, cast).
-// The library keeps no state between calls.
+// The library allocates nothing and keeps no state between calls.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdio.h>
@@ -14,6 +17,10 @@
 
 #include "attn_bwd.h"
 #include "kernels.h"
+
+#ifndef ATTN_TOPK_MASK_MAX
+#define ATTN_TOPK_MASK_MAX ((int64_t)1 << 30)  // bytes of the top-k key-count mask
+#endif
 
 namespace {
 
@@ -55,6 +62,8 @@ int validate_sizes(const attn_bwd_args *a) {
   if (a->B * a->Sq * a->Hq >= lim || a->B * a->Skv * a->Hkv >= lim) return ATTN_E_UNSUPPORTED;
   if (a->topk_idx) {
     if (a->topk > 65535) return ATTN_E_UNSUPPORTED;  // 16-bit key counts
+    // The key-count mask holds one 16-bit count per (batch, KV head, query, key).
+    if (a->B * a->Hkv * a->Sq * ((a->Skv + 31) / 32 * 32) * 2 > ATTN_TOPK_MASK_MAX) return ATTN_E_UNSUPPORTED;
     if (!(a->Dqk == 576 && a->Dv == 512)) return ATTN_E_UNSUPPORTED;
     // The gathers address one (batch, KV head)'s K or V rows with 32-bit byte offsets.
     if (a->Skv * a->Hkv * a->Dqk * 2 >= ((int64_t)1 << 32)) return ATTN_E_UNSUPPORTED;
@@ -67,8 +76,8 @@ int validate_sizes(const attn_bwd_args *a) {
 // Workspace, each part 256-byte aligned: delta [B,Hq,Sq] f32, the sanitised lse [B,Hq,Sq] f32,
 // and for the top-k path the accumulators dK_acc [B,Skv,Hkv,Dqk] and dV_acc [B,Skv,Hkv,Dv] f32
 // and the key counts cnt [B,Hkv,Sq,skv_pad] u16 (skv_pad = Skv rounded up to 32).  Packed calls
-// and dense GQA calls on the dK/dV work queue: [dK_acc, dV_acc when the head group is split,] then
-// the queue counter.
+// on the dK/dV work queue: [two f32 slices each of dK and dV, [T,Hkv,D], when the head group is
+// split,] then the queue counter.
 size_t row_stat_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Hq * a->Sq) * sizeof(float)); }
 size_t dk_acc_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Skv * a->Hkv * a->Dqk) * 4); }
 size_t dv_acc_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Skv * a->Hkv * a->Dv) * 4); }
@@ -79,20 +88,18 @@ size_t cnt_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Hk
 #endif
 // dK/dV work queue.  Packed calls without a window take their key blocks from a device counter:
 // their lengths differ, so a fixed block-to-CU mapping leaves CUs idle behind the longest
-// sequence.  When the head group splits in two, each item holds one half, and the halves add
-// their blocks into f32 accumulators [B*Skv, Hkv, D] for dK and dV; two adds onto zero give the
-// same sum in either order, so the result stays deterministic.  Dense calls without a window
-// take the queue with the split when the head group has 8 heads or more (16K GQA with 8: dK/dV
-// 3.4% faster); the MHA headline ran 7% slower on the queue without a split.
+// sequence.  When the head group splits in two, each item holds one half and stores its f32
+// block with plain stores into its own slice [T, Hkv, D]; the landing pass adds slice 0 and
+// slice 1 in that order, so the result is deterministic and no atomics are involved.  Dense
+// batches keep one workgroup per key block, which stores dK/dV once at Hkv.
 bool dkdv_queue(const attn_bwd_args *a) {
-  if (!ATTN_PACKED_QUEUE || a->topk_idx || a->window != 0) return false;
-  const int64_t G = a->Hq / a->Hkv;
-  return a->cu_seqlens || (G >= 8 && G % 2 == 0);
+  return ATTN_PACKED_QUEUE && a->cu_seqlens && !a->topk_idx && a->window == 0;
 }
 int dkdv_hsplit(const attn_bwd_args *a) { return dkdv_queue(a) && (a->Hq / a->Hkv) % 2 == 0 ? 2 : 1; }
+size_t part_bytes(const attn_bwd_args *a) { return align256((size_t)(a->B * a->Skv * a->Hkv * a->Dqk) * 4 * 2); }
 size_t queue_bytes(const attn_bwd_args *a) {
   if (!dkdv_queue(a)) return 0;
-  return 256 + (dkdv_hsplit(a) > 1 ? dk_acc_bytes(a) + dv_acc_bytes(a) : 0);
+  return 256 + (dkdv_hsplit(a) > 1 ? 2 * part_bytes(a) : 0);
 }
 size_t workspace_bytes_for(const attn_bwd_args *a) {
   size_t n = 2 * row_stat_bytes(a);
@@ -137,40 +144,24 @@ int run_fwd(const void *q, const void *k, const void *v, void *o, float *lse, in
   return ATTN_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t attn_bwd_workspace_size(const attn_bwd_args *a) {
-  if (validate_sizes(a) != ATTN_OK) return 0;
-  return workspace_bytes_for(a);
-}
-
-int attn_bwd_ex(const attn_bwd_args *a) {
-  int rc = validate_sizes(a);
-  if (rc != ATTN_OK) return rc;
-  // Shared-latent form: V is read from k and dV is added into dk, so v and dv must be NULL.
+// Pointer and flag checks of a call (after validate_sizes): non-null, aligned inputs and outputs;
+// in the shared-latent form v and dv must be NULL (V is read from k, dV is added into dk).
+int validate_ptrs(const attn_bwd_args *a) {
   const bool shared = a->kv_shared != 0;
   if (shared && (a->v || a->dv)) return ATTN_E_INVAL;
   const void *ptrs[] = {a->q, a->k, shared ? a->k : a->v, a->o, a->dout, a->lse, a->dq, a->dk, shared ? a->dk : a->dv};
   for (const void *p : ptrs)
     if (!p || !aligned16(p)) return ATTN_E_INVAL;
   if (a->topk_idx && ((uintptr_t)a->topk_idx & 3) != 0) return ATTN_E_INVAL;
-  const size_t need = workspace_bytes_for(a);
-  if (a->workspace) {
-    if (((uintptr_t)a->workspace & 255) != 0) return ATTN_E_INVAL;
-    if (a->workspace_bytes < need) return ATTN_E_WORKSPACE;
-  } else if (a->workspace_bytes != 0) {
-    return ATTN_E_INVAL;
-  }
+  return ATTN_OK;
+}
 
+// The backward on a validated argument set, with `ws` a device workspace of at least
+// workspace_bytes_for(a) bytes, 256-byte aligned.
+int run_bwd(const attn_bwd_args *a, void *ws) {
+  const bool shared = a->kv_shared != 0;
   hipStream_t st = (hipStream_t)a->stream;
   const bool bf16 = a->dtype == ATTN_DT_BF16;
-  void *ws = a->workspace;
-  if (!ws) {
-    hipError_t e = hipMallocAsync(&ws, need, st);
-    if (e != hipSuccess) return set_hip_error(e, "hipMallocAsync(workspace)");
-  }
 
   attn::Params p;
   p.q = (const short *)a->q;
@@ -216,18 +207,16 @@ int attn_bwd_ex(const attn_bwd_args *a) {
       p.hsplit = dkdv_hsplit(a);
       if (p.hsplit > 1) {
         p.dk_acc = (float *)qb;
-        p.dv_acc = (float *)(qb + dk_acc_bytes(a));
+        p.dv_acc = (float *)(qb + part_bytes(a));
+        p.acc_slice = a->B * a->Skv * a->Hkv * a->Dqk;
       }
       p.work = (int *)(qb + queue_bytes(a) - 256);
-      if (e == hipSuccess) e = attn::launch_zero((float *)qb, (int64_t)(queue_bytes(a) / 4), st);
+      // Only the counter starts at zero: every slice row inside a sequence is stored by its item.
+      if (e == hipSuccess) e = attn::launch_zero((float *)p.work, 64, st);
     }
     if (e == hipSuccess) e = attn::launch_dense_dkdv(p, bf16, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
-    if (p.hsplit > 1) {
-      const int64_t nk = a->B * a->Skv * a->Hkv * a->Dqk;
-      if (e == hipSuccess) e = attn::launch_land(p.dk_acc, p.dk, nk, a->scale, bf16, st);
-      if (e == hipSuccess) e = attn::launch_land(p.dv_acc, p.dv, nk, 1.0f, bf16, st);
-    }
+    if (p.hsplit > 1 && e == hipSuccess) e = attn::launch_land_parts(p, bf16, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
   } else {
     if (e == hipSuccess)
@@ -254,12 +243,28 @@ int attn_bwd_ex(const attn_bwd_args *a) {
     }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
   }
-  if (!a->workspace) {
-    hipError_t e2 = hipFreeAsync(ws, st);
-    if (e == hipSuccess && e2 != hipSuccess) return set_hip_error(e2, "hipFreeAsync(workspace)");
-  }
   if (e != hipSuccess) return set_hip_error(e, "kernel launch");
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_workspace_size(const attn_bwd_args *a) {
+  if (validate_sizes(a) != ATTN_OK) return 0;
+  return workspace_bytes_for(a);
+}
+
+int attn_bwd_ex(const attn_bwd_args *a) {
+  int rc = validate_sizes(a);
+  if (rc == ATTN_OK) rc = validate_ptrs(a);
+  if (rc != ATTN_OK) return rc;
+  // The caller provides the workspace (the library allocates nothing).
+  const size_t need = workspace_bytes_for(a);
+  if (!a->workspace || a->workspace_bytes < need) return ATTN_E_WORKSPACE;
+  if (((uintptr_t)a->workspace & 255) != 0) return ATTN_E_INVAL;
+  return run_bwd(a, a->workspace);
 }
 
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse, void *dq,

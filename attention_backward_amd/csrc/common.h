@@ -43,10 +43,11 @@ struct Params {
   float c;                            // scale * log2(e)
   const int32_t *cu;                  // packed sequences: [nseq + 1] token offsets, or null
   int nseq, max_seqlen;               // packed sequences: their number and a bound on each length
-  int hsplit = 1;                     // dense dK/dV: items sharing one key block's query heads
-  float *dk_acc = nullptr;            // hsplit > 1: zeroed f32 [tokens, Hkv, D] the parts add into
-  float *dv_acc = nullptr;
-  int *work = nullptr;                // dense dK/dV work-queue counter (zeroed), or null
+  int hsplit = 1;                     // packed dK/dV: items sharing one key block's query heads
+  float *dk_acc = nullptr;            // hsplit > 1: f32 [hsplit][tokens, Hkv, D] slices, one per
+  float *dv_acc = nullptr;            //   part (plain stores; the landing pass adds them)
+  int64_t acc_slice = 0;              // elements per slice (tokens * Hkv * D)
+  int *work = nullptr;                // dK/dV work-queue counter (zeroed), or null
 };
 
 // The sequence one workgroup works on.  Dense: batch s of equal-length sequences.  Packed (cu not

@@ -6,7 +6,10 @@
 // once, cast to the input dtype, with the softmax scale applied to dK at the end.  For GQA the
 // workgroup walks all G query heads of its KV head for every query block, so dK/dV are written
 // directly at Hkv heads with no Hq-shaped intermediate and no atomics (flash-linear-attention
-// issue #8, the KV-head-owned kernel it proposes).
+// issue #8, the KV-head-owned kernel it proposes).  Packed sequences without a window take the
+// work-queue form below; with an even head group each key block is then split into two items
+// (half the group's heads each), which store their f32 blocks into two separate Hkv-shaped slices
+// that a landing pass adds in a fixed order and casts -- still no atomics, and deterministic.
 //
 // CDNA4 layout of one workgroup (512 threads = 8 wave64s, two per SIMD, 128 keys):
 //   waves 0..3 ("P role")  own keys [k0 + 32w, +32): hold those K rows in registers as MFMA
@@ -87,7 +90,7 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
   const int hi = lane >> 5, lo = lane & 31;
   const int i16 = lane & 15, g16 = lane >> 4;
   // hsplit items share a key block: part sp walks query heads [sp * Gs, (sp + 1) * Gs) of the KV
-  // head's group and adds its finished block into f32 accumulators.
+  // head's group and stores its finished f32 block into its own slice.
   const int BH = (p.cu ? p.nseq : p.B) * p.Hkv * p.hsplit;
   const int kb = item / BH;
   // Packed sequences without a window: rotate the (sequence, head) index by the key block.
@@ -337,15 +340,17 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
 
   // Epilogue: dV (P role) or scale * dK (dS role), cast once, BSHD at the KV head.
   const float sc = role == 0 ? 1.f : p.scale;
-  if (p.hsplit > 1) {  // one f32 add per element of this part's block (two parts: either order)
-    float *acc_out = role == 0 ? p.dv_acc : p.dk_acc;
+  if (p.hsplit > 1) {
+    // Part sp of the head group stores its unscaled f32 block with plain stores into its own
+    // slice [sp][tokens, Hkv, D]; the landing pass adds the slices in a fixed order.
+    float *acc_out = (role == 0 ? p.dv_acc : p.dk_acc) + (int64_t)sp * p.acc_slice;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const int key = kbase + 8 * (r >> 2) + 4 * hi + (r & 3);
       if (key < Skv) {
         float *row = acc_out + ((sv.k0 + key) * p.Hkv + g) * D + lo;
 #pragma unroll
-        for (int dn = 0; dn < C::ND; dn++) unsafeAtomicAdd(&row[32 * dn], acc[dn][r]);
+        for (int dn = 0; dn < C::ND; dn++) row[32 * dn] = acc[dn][r];
       }
     }
     return;
@@ -401,6 +406,49 @@ static hipError_t launch_dkdv_t(const Params &p, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((dense_dkdv_kernel<TT, D, BN>), dim3((unsigned)items), dim3(512), 0, st, p);
   }
+  return hipGetLastError();
+}
+
+// Landing of the split dK/dV (packed calls): dk = DT(scale * (slice 0 + slice 1)), dv = DT(slice 0
+// + slice 1), the two slices always added in that order.  Only the rows of each sequence (clamped
+// like the kernels' SeqView) are written, so tokens outside every sequence keep their contents.
+// Thread: 8 consecutive elements of one sequence's [rows, Hkv, D] block.
+template <class TT>
+__global__ __launch_bounds__(256) void land_parts_kernel(const Params p, int64_t bps) {
+  const int s = (int)(blockIdx.x / bps);
+  const int64_t c8 = (int64_t)(blockIdx.x % bps) * 256 + threadIdx.x;
+  const SeqView sv = seq_view(p.cu, s, p.Sq, p.Skv, p.Hq, p.max_seqlen);
+  const int64_t row_elems = (int64_t)p.Hkv * p.Dqk;
+  if (8 * c8 >= sv.Skv * row_elems) return;
+  const int64_t e = sv.k0 * row_elems + 8 * c8;
+  const float *acc[2] = {p.dk_acc, p.dv_acc};
+  short *out[2] = {p.dk, p.dv};
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const float *a0 = acc[t] + e, *a1 = acc[t] + p.acc_slice + e;
+    const float sc = t == 0 ? p.scale : 1.f;
+    const f4v x0 = *(const f4v *)a0 + *(const f4v *)a1;
+    const f4v x1 = *(const f4v *)(a0 + 4) + *(const f4v *)(a1 + 4);
+    s8v o;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      o[i] = TT::cvt(x0[i] * sc);
+      o[4 + i] = TT::cvt(x1[i] * sc);
+    }
+    *(s8v *)(out[t] + e) = o;
+  }
+}
+
+hipError_t launch_land_parts(const Params &p, bool bf16, hipStream_t st) {
+  if (!p.cu || p.hsplit != 2 || (p.Hkv * p.Dqk) % 8 != 0) return hipErrorInvalidValue;
+  const int64_t bps = ((int64_t)p.max_seqlen * p.Hkv * p.Dqk / 8 + 255) / 256;
+  const int64_t blocks = bps * p.nseq;
+  if (blocks < 1) return hipSuccess;
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (bf16)
+    hipLaunchKernelGGL(land_parts_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, p, bps);
+  else
+    hipLaunchKernelGGL(land_parts_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, p, bps);
   return hipGetLastError();
 }
 

@@ -15,6 +15,9 @@ hipError_t launch_delta(const short *o, const short *dout, float *delta, const f
 // Dense path, D = Dqk = Dv in {64, 128}: dK/dV (KV-block owned) and dQ (query-block owned).
 hipError_t launch_dense_dkdv(const Params &p, bool bf16, hipStream_t st);
 hipError_t launch_dense_dq(const Params &p, bool bf16, hipStream_t st);
+// Packed calls with the head group split in two (p.hsplit = 2): dk/dv = DT(slice 0 + slice 1) of
+// the f32 dK/dV slices, over the rows of each sequence only.
+hipError_t launch_land_parts(const Params &p, bool bf16, hipStream_t st);
 
 // Arguments of the forward kernel (O and the base-2 lse from Q, K, V).
 struct FwdParams {

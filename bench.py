@@ -384,7 +384,8 @@ def bench_varlen(args, vw, ab):
         flops, kname, kflops = fwd_flops, "dense_fwd", fwd_flops
     else:
         per = {"dq": [row[0].elapsed_time(row[1]) * 1e3 for row in ev],
-               "dkdv": [row[1].elapsed_time(row[2]) * 1e3 for row in ev]}
+               "dkdv": [row[1].elapsed_time(row[2]) * 1e3 for row in ev],
+               "landing": [row[2].elapsed_time(row[3]) * 1e3 for row in ev]}
         flops, kname, kflops = 2.5 * fwd_flops, "dense_dkdv", npairs * 8 * vw.D
     kus = statistics.fmean(per["fwd" if args.forward else "dkdv"])
     ktf = kflops / (kus * 1e-6) / 1e12
@@ -413,6 +414,14 @@ def bench_varlen(args, vw, ab):
                      "algorithmic_flops_per_launch": kflops},
         "kernels_us_median": {n_: round(statistics.median(x), 2) for n_, x in per.items()},
     }
+    if not args.forward and vw.window == 0 and (vw.Hq // vw.Hkv) % 2 == 0:
+        # The split dK/dV: the landing pass reads two f32 slices each of dK and dV and writes dk, dv
+        # over the tokens of the sequences.
+        ntok = int(sum(min(int(n), mx) for n in lens))
+        land_bytes = ntok * vw.Hkv * vw.D * (2 * 2 * 4 + 2 * 2)
+        lus = statistics.fmean(per["landing"])
+        result["landing"] = {"us": round(lus, 2), "GB/s": round(land_bytes / (lus * 1e-6) / 1e9, 1),
+                             "frac_of_hbm_peak": round(land_bytes / (lus * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     print(json.dumps(result), flush=True)
 
 

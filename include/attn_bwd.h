@@ -60,13 +60,14 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_E_INVAL = -1,        /* a null/misaligned pointer, a negative size, Hq % Hkv != 0, ... */
   ATTN_E_UNSUPPORTED = -2,  /* a valid request this build has no kernel for (head dims, dtype) */
-  ATTN_E_WORKSPACE = -3,    /* workspace_bytes smaller than attn_bwd_workspace_size()         */
+  ATTN_E_WORKSPACE = -3,    /* workspace NULL or smaller than attn_bwd_workspace_size()       */
   ATTN_E_HIP = -4           /* a HIP runtime call or kernel launch failed                      */
 } attn_status;
 
 /* Full argument set.  Sizes are int64; Sq != Skv and Dqk != Dv are allowed where a kernel
  * exists: dense (Dqk, Dv) in {(64,64), (128,128)}; top-k (Dqk, Dv) = (576, 512) with
- * Skv * Hkv * Dqk * 2 < 2^32 (ATTN_E_UNSUPPORTED otherwise). */
+ * Skv * Hkv * Dqk * 2 < 2^32, topk <= 65535 and a key-count mask of B * Hkv * Sq * (Skv rounded
+ * up to 32) 16-bit counts of at most 1 GiB (ATTN_E_UNSUPPORTED otherwise). */
 typedef struct {
   const void *q, *k, *v, *o, *dout; /* 16-byte aligned device pointers, element type = dtype   */
   const float *lse;                 /* [B, Hq, Sq] float32, base-2 log-sum-exp of the forward   */
@@ -77,16 +78,18 @@ typedef struct {
   int32_t causal;                   /* 0 or 1                                                  */
   int32_t window;                   /* 0 = no window; > 0 requires causal = 1 and no topk_idx  */
   int32_t dtype;                    /* attn_dtype                                              */
-  void *workspace;                  /* device scratch of workspace_bytes, 256-byte aligned, or
-                                       NULL with workspace_bytes = 0: the library then takes
-                                       stream-ordered memory (hipMallocAsync/hipFreeAsync)     */
+  void *workspace;                  /* caller-allocated device scratch of workspace_bytes, 256-byte
+                                       aligned, at least attn_bwd_workspace_size() bytes; NULL or
+                                       a smaller size returns ATTN_E_WORKSPACE (the library
+                                       allocates nothing)                                        */
   size_t workspace_bytes;
   void *stream;                     /* hipStream_t                                             */
   void *events;                     /* optional, NULL or an array of 4 hipEvent_t created by the
                                        caller, recorded on `stream` between the phases: dense =
                                        before the dQ kernel (which also forms delta and the lse
-                                       copy) | after it | after the dK/dV kernel | again after
-                                       the dK/dV kernel; top-k = before the preprocess | after
+                                       copy) | after it | after the dK/dV kernel | after the
+                                       landing pass of a split packed call (else again after
+                                       the dK/dV kernel); top-k = before the preprocess | after
                                        it, the zero-fill, the key counts and the dQ kernel |
                                        after the dK/dV kernel | after the landing passes
                                        (per-phase timing without changing the work)          */
@@ -118,14 +121,16 @@ typedef struct {
  * 256-byte aligned parts:
  *   delta (stored negated) and a sanitised copy of lse, [B,Hq,Sq] f32 each;
  *   top-k only: f32 accumulators dK_acc [B,Skv,Hkv,Dqk] and dV_acc [B,Skv,Hkv,Dv] and the
- *   16-bit key counts;
- *   without a window, packed sequences, and dense calls with Hq / Hkv >= 8 and even: f32 dK/dV
- *   accumulators [B*Skv,Hkv,D] each when Hq / Hkv is even (the two halves of each head group
- *   add into them: two adds onto zero, so the result is still identical between calls), then
- *   256 bytes for the dK/dV work-queue counter.
- * Never an Hq-shaped dK/dV buffer.  Top-k results: dq is written once per element; dk and dv
- * (or dKV in the shared-latent form) are sums of f32 atomic additions, so their last bits may
- * differ between identical calls.  The shared-latent form needs the same workspace. */
+ *   16-bit key counts [B,Hkv,Sq,Skv rounded up to 32];
+ *   packed sequences without a window: when Hq / Hkv is even, two f32 slices each of dK and dV,
+ *   [T,Hkv,D] (each half of a head group stores its block into its own slice with plain stores,
+ *   and a landing pass adds slice 0 and slice 1 in that order), then 256 bytes for the dK/dV
+ *   work-queue counter.
+ * Never an Hq-shaped dK/dV buffer, and no atomics on the dense dK/dV.  Dense results (dq, dk, dv)
+ * are identical between identical calls.  Top-k results: dq is written once per element; dk and
+ * dv (or dKV in the shared-latent form) are sums of f32 atomic additions (one per key block and
+ * query chunk), so their last bits may differ between identical calls.  The shared-latent form
+ * needs the same workspace. */
 size_t attn_bwd_workspace_size(const attn_bwd_args *a);
 
 /* The backward for the full argument set.  Returns an attn_status. */

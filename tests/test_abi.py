@@ -45,10 +45,10 @@ def test_workspace_size():
     assert ab.attn_bwd_workspace_size(valid_args()) == 2 * (2 * 32 * 2048 * 4)
     # never Hq-shaped dK/dV: a head group of 2 or 4 needs the same delta-only workspace
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=8)) == 2 * (2 * 32 * 2048 * 4)
-    # a head group of 8 or more, no window: the dK/dV work queue, with f32 dK/dV accumulators
-    # at Hkv for its two halves and 256 bytes for the counter
-    acc = 2 * 2048 * 4 * 128 * 4
-    assert ab.attn_bwd_workspace_size(valid_args(Hkv=4)) == 2 * (2 * 32 * 2048 * 4) + 2 * acc + 256
+    # dense batches store dK/dV once at Hkv from one workgroup per key block, whatever the head
+    # group: no f32 dK/dV accumulators and no work-queue counter
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=4)) == 2 * (2 * 32 * 2048 * 4)
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=1)) == 2 * (2 * 32 * 2048 * 4)
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=4, window=64)) == 2 * (2 * 32 * 2048 * 4)
     assert ab.attn_bwd_workspace_size(valid_args(B=1, Sq=3, Hq=2, Hkv=2)) == 512  # 256-byte granularity
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=5)) == 0
@@ -85,6 +85,10 @@ def test_workspace_size():
         (dict(topk_idx=0x100000, topk=65536, Dqk=576, Dv=512), -2),  # key counts are 16-bit
         # gathers use 32-bit byte offsets within one (batch, KV head)'s K rows
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, Skv=1 << 22, Hkv=1, Hq=64), -2),
+        # the 16-bit key-count mask [B,Hkv,Sq,Skv rounded up to 32] is bounded at 1 GiB
+        (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, B=1, Sq=16384, Skv=32769, Hkv=1, Hq=64), -2),
+        (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, B=1, Sq=16384, Skv=32768, Hkv=1, Hq=64,
+              workspace=0x100000, workspace_bytes=16), -3),  # exactly 1 GiB: valid up to the workspace
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, workspace=0x100000, workspace_bytes=1 << 20), -3),
         (dict(workspace=0x100000, workspace_bytes=16), -3),
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, kv_shared=2), -1),
@@ -94,7 +98,9 @@ def test_workspace_size():
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, kv_shared=1, v=0, dv=0, workspace=0x100000,
               workspace_bytes=16), -3),
         (dict(workspace=0x100080, workspace_bytes=1 << 30), -1),  # workspace not 256-byte aligned
-        (dict(workspace=0, workspace_bytes=64), -1),
+        # the library allocates nothing: a call without a workspace is refused
+        (dict(workspace=0, workspace_bytes=0), -3),
+        (dict(workspace=0, workspace_bytes=1 << 30), -3),
         # packed sequences: a batch of one on the dense path
         (dict(PACKED, B=2), -1),
         (dict(PACKED, Skv=4000), -1),
@@ -177,11 +183,12 @@ def test_forward_varlen_entry_point_validates(kw, status):
 
 
 def test_packed_workspace():
-    """delta and lse as for the batch of one; without a window, f32 dK/dV accumulators when the
-    head group (here 32 / 8) splits in two halves, then 256 bytes for the dK/dV work-queue
-    counter."""
+    """delta and lse as for the batch of one; without a window, two f32 [T,Hkv,D] slices each of
+    dK and dV when the head group (here 32 / 8) splits in two halves, then 256 bytes for the
+    dK/dV work-queue counter."""
     acc = 4096 * 8 * 128 * 4
-    assert ab.attn_bwd_workspace_size(valid_args(**dict(PACKED, Hkv=8))) == 2 * (32 * 4096 * 4) + 2 * acc + 256
+    assert ab.attn_bwd_workspace_size(valid_args(**dict(PACKED, Hkv=8))) == 2 * (32 * 4096 * 4) + 4 * acc + 256
+    assert ab.attn_bwd_workspace_size(valid_args(**dict(PACKED, Hkv=16))) == 2 * (32 * 4096 * 4) + 8 * acc + 256
     # a head group of one cannot split: the counter only
     assert ab.attn_bwd_workspace_size(valid_args(**PACKED)) == 2 * (32 * 4096 * 4) + 256
     assert ab.attn_bwd_workspace_size(valid_args(**dict(PACKED, window=100))) == 2 * (32 * 4096 * 4)

@@ -65,6 +65,8 @@ SMALL = [
     small("swa_g8_d128_window37", B=1, Sq=333, Skv=333, Hq=8, Hkv=1, window=37, seed=106),
     small("swa_window1024_t2500", B=1, Sq=2500, Skv=2500, Hq=4, Hkv=2, Dqk=64, Dv=64, window=1024, seed=107),
     small("mha_causal_s1024_h4_bf16", Sq=1024, Skv=1024, Hq=4, Hkv=4, dtype="bf16", seed=108),
+    small("gqa_g8_nowindow_ragged_fp16", Sq=333, Skv=333, Hq=8, Hkv=1, seed=109),
+    small("gqa_g8_nowindow_ragged_bf16", B=2, Sq=397, Skv=397, Hq=16, Hkv=2, dtype="bf16", seed=110),
 ] + [small(f"tiny_s{s}", Sq=s, Skv=s, seed=110 + s) for s in (1, 2, 63, 65, 127, 129, 200)]
 
 
@@ -73,8 +75,14 @@ def test_small_full_parity(w):
     full_compare(w)
 
 
-def test_deterministic_and_both_entry_points():
-    w = SMALL[1]
+DET = [SMALL[1], SMALL[-2], SMALL[-1]]  # G = 4; G = 8 without a window, fp16 and bf16
+
+
+@pytest.mark.parametrize("w", DET, ids=[w.name for w in DET])
+def test_deterministic_and_both_entry_points(w):
+    """Two identical calls give the same bits (dense dK/dV are stored once, dQ is owned), and so
+    does the plain-argument entry point with a caller-allocated workspace."""
+    log(f"case {w.name} (bit identity)")
     inp = prepare(w)
     a = run(inp, w)
     b = run(inp, w)
@@ -83,11 +91,20 @@ def test_deterministic_and_both_entry_points():
     # the plain-argument entry point gives the same bits
     g = to_gpu(inp)
     dq, dk, dv = poisoned_like(g["q"]), poisoned_like(g["k"]), poisoned_like(g["v"])
+    args = ab.make_args(g["q"], g["k"], g["v"], g["o"], g["dout"], g["lse"], dq, dk, dv, scale=w.scale,
+                        causal=w.causal, window=w.window)
+    need = ab.attn_bwd_workspace_size(args)
+    ws = poisoned_like(torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda"))
     ab.attn_bwd(g["q"], g["k"], g["v"], g["o"], g["dout"], g["lse"], dq, dk, dv, w.B, w.Sq, w.Hq, w.Hkv, w.Dqk,
-                w.scale, w.causal, w.window)
+                w.scale, w.causal, w.window, workspace=ws, workspace_bytes=need)
     torch.cuda.synchronize()
     for x, y in zip(a, (dq.cpu(), dk.cpu(), dv.cpu())):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    # without a workspace the call is refused before anything is enqueued
+    with pytest.raises(ab.AttnBwdError) as e:
+        ab.attn_bwd(g["q"], g["k"], g["v"], g["o"], g["dout"], g["lse"], dq, dk, dv, w.B, w.Sq, w.Hq, w.Hkv, w.Dqk,
+                    w.scale, w.causal, w.window)
+    assert e.value.status == ab._lib.ATTN_E_WORKSPACE
 
 
 @pytest.mark.parametrize("dtype,Dv", [("fp16", 128), ("bf16", 64), ("bf16", 512), ("fp16", 256)])

@@ -87,9 +87,9 @@ def test_varlen_small_full_parity(w):
 def test_single_packed_sequence_is_the_dense_batch_of_one():
     """Same kernels, same per-row arithmetic: a packed call holding one sequence gives the bits of
     the dense call with B = 1 for O, lse and dQ.  dK and dV differ in rounding only: the packed
-    call splits each head group into two halves whose f32 sums add into zeroed accumulators, where
-    the dense call sums the whole group in one workgroup.  Both halves add onto zero, in either
-    order the same sum, so repeated packed calls agree bit for bit."""
+    call splits each head group into two halves whose f32 blocks go to two slices that the landing
+    pass adds in a fixed order, where the dense call sums the whole group in one workgroup.
+    Repeated packed calls agree bit for bit."""
     w = vw("vl_one", (777,), 4, 2, 128, "fp16", True, 0, 410)
     inp = synth.make_varlen_inputs(w)
     _, _, o_st, lse32 = oracle_o_lse(inp, w)
@@ -167,3 +167,27 @@ def test_varlen_full_size_sampled_parity(name):
     check_close("dv rows", dv[0, krows[:, 1], krows[:, 2]].double().numpy(), np.array([r[1] for r in kr]))
     for t in (go, glse, dq, dk, dv):
         assert torch.isfinite(t.float()).all()
+
+
+@pytest.mark.parametrize("Hq,Hkv,dtype", [(4, 2, "fp16"), (3, 1, "bf16"), (16, 2, "bf16")],
+                         ids=["g2_split_fp16", "g3_odd_bf16", "g8_split_bf16"])
+def test_tokens_outside_every_sequence_keep_their_contents(Hq, Hkv, dtype):
+    """Offsets ending before T (cu[nseq] < T) and a sequence longer than max_seqlen: the kernels
+    (and, for an even head group, the landing of the two f32 halves) write only the rows each
+    sequence covers, cut at max_seqlen, so the rows past them keep the poison.  The rows written
+    match the oracle over the sequences as cut, and a second call gives the same bits."""
+    w = vw(f"vl_outside_{Hq}_{Hkv}", (200, 250, 150), Hq, Hkv, 128, dtype, True, 0, 420 + Hq)
+    inp = synth.make_varlen_inputs(w)
+    inp["cu"] = torch.tensor([0, 200, 450], dtype=torch.int32)   # tokens 450..599: no sequence
+    inp["max_seqlen"] = 230                                        # sequence 1 is cut at token 430
+    log(f"packed case {w.name}: cu={inp['cu'].tolist()} T={w.T} max_seqlen=230 {dtype}")
+    cut = torch.tensor([0, 200, 430], dtype=torch.int32)
+    _, _, o_st, lse32 = oracle_o_lse(dict(inp, cu=cut), w)
+    dq, dk, dv = gpu_bwd(inp, o_st, lse32, w)
+    again = gpu_bwd(inp, o_st, lse32, w)
+    for x, y in zip((dq, dk, dv), again):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16)), "two identical packed calls differ"
+    ref = oracle.bwd_varlen(inp["q"], inp["k"], inp["v"], o_st, inp["dout"], lse32, cut, w.scale, True, 0)
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        check_close(name, got[:, :430].double().numpy(), r[:, :430])
+        assert torch.all(got[:, 430:].view(torch.int16) == -1), f"{name}: rows outside every sequence were written"
