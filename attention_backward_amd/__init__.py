@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     attn_bwd_args,
     attn_bwd_delta,
     attn_bwd_ex,
+    attn_bwd_noalloc,
     attn_bwd_strerror,
     attn_bwd_workspace_size,
     attn_fwd,

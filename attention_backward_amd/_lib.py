@@ -19,8 +19,9 @@ ATTN_DT_F16, ATTN_DT_BF16 = 0, 1
 ATTN_OK, ATTN_E_INVAL, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = 0, -1, -2, -3, -4
 _DT = {torch.float16: ATTN_DT_F16, torch.bfloat16: ATTN_DT_BF16}
 
-EXPORTS = ("attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_size", "attn_bwd_delta", "attn_fwd",
+EXPORTS = ("attn_bwd", "attn_bwd_ex", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_bwd_delta", "attn_fwd",
            "attn_fwd_varlen", "attn_bwd_strerror")
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_NOALLOC_SCRATCH_BYTES of include/attn_bwd.h
 
 
 class attn_bwd_args(ctypes.Structure):  # noqa: N801  (mirrors the C struct name)
@@ -63,6 +64,8 @@ def load() -> ctypes.CDLL:
         lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
         lib.attn_bwd_ex.argtypes = [ctypes.POINTER(attn_bwd_args)]
         lib.attn_bwd_ex.restype = ctypes.c_int
+        lib.attn_bwd_noalloc.argtypes = [ctypes.POINTER(attn_bwd_args)]
+        lib.attn_bwd_noalloc.restype = ctypes.c_int
         lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I32, I32, P, I64,
                                  I32, P, ctypes.c_size_t, P]
         lib.attn_bwd.restype = ctypes.c_int
@@ -157,6 +160,11 @@ def attn_bwd_workspace_size(args: attn_bwd_args) -> int:
 
 def attn_bwd_ex(args: attn_bwd_args) -> None:
     _check(load().attn_bwd_ex(ctypes.byref(args)))
+
+
+def attn_bwd_noalloc(args: attn_bwd_args) -> None:
+    """attn_bwd_ex on the library's static per-device scratch (args.workspace is ignored)."""
+    _check(load().attn_bwd_noalloc(ctypes.byref(args)))
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, S, Hq, Hkv, D, scale, causal, window, topk_idx=None, topk=0,

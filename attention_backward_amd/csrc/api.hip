@@ -15,6 +15,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "attn_bwd.h"
 #include "kernels.h"
 
@@ -247,6 +249,35 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
   return ATTN_OK;
 }
 
+// Device scratch of attn_bwd_noalloc: one file-scope array that each GPU the library runs on
+// holds until the process ends.  Host code never uses its name as an address (on the host it is
+// only a stand-in for the symbol); it takes the device address once per device, with that device
+// current, from hipGetSymbolAddress, and passes that pointer to the kernels.
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The scratch address on the current device (set up on its first call there), or an error.
+int scratch_for_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_hip_error(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return set_hip_error(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || ((uintptr_t)ptr & 255) != 0) return set_hip_error(hipErrorInvalidSymbol, "scratch address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -265,6 +296,17 @@ int attn_bwd_ex(const attn_bwd_args *a) {
   if (!a->workspace || a->workspace_bytes < need) return ATTN_E_WORKSPACE;
   if (((uintptr_t)a->workspace & 255) != 0) return ATTN_E_INVAL;
   return run_bwd(a, a->workspace);
+}
+
+int attn_bwd_noalloc(const attn_bwd_args *a) {
+  int rc = validate_sizes(a);
+  if (rc == ATTN_OK) rc = validate_ptrs(a);
+  if (rc != ATTN_OK) return rc;
+  if (workspace_bytes_for(a) > kScratchBytes) return ATTN_E_WORKSPACE;
+  void *ws = nullptr;
+  rc = scratch_for_current_device(&ws);
+  if (rc != ATTN_OK) return rc;
+  return run_bwd(a, ws);
 }
 
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse, void *dq,
@@ -337,7 +379,8 @@ const char *attn_bwd_strerror(int status) {
     case ATTN_E_UNSUPPORTED:
       return "unsupported: no kernel for this head-dim / variant in this build";
     case ATTN_E_WORKSPACE:
-      return "workspace smaller than attn_bwd_workspace_size()";
+      return "workspace missing or smaller than attn_bwd_workspace_size() (attn_bwd_ex), or the call needs more "
+             "than ATTN_NOALLOC_SCRATCH_BYTES of static scratch (attn_bwd_noalloc)";
     case ATTN_E_HIP:
       return g_msg[0] ? g_msg : "HIP runtime error";
     default:

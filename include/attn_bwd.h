@@ -136,6 +136,20 @@ size_t attn_bwd_workspace_size(const attn_bwd_args *a);
 /* The backward for the full argument set.  Returns an attn_status. */
 int attn_bwd_ex(const attn_bwd_args *a);
 
+/* The backward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): attn_bwd_ex with the workspace taken
+ * from a static device array of ATTN_NOALLOC_SCRATCH_BYTES that each GPU the library runs on
+ * holds until the process ends; a->workspace and a->workspace_bytes are ignored.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine); on its first call on a
+ * device it looks up that device's copy of the array.  Arguments, validation and results are
+ * those of attn_bwd_ex; a call whose attn_bwd_workspace_size() exceeds
+ * ATTN_NOALLOC_SCRATCH_BYTES returns ATTN_E_WORKSPACE before anything is enqueued.  Every call
+ * on one GPU shares that GPU's array (the kernels clear what must start at zero), so calls that
+ * overlap on one GPU -- on different streams or from different threads -- race and must be
+ * ordered by the caller. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_bwd_noalloc(const attn_bwd_args *a);
+
 /* The same operation with Sq = Skv = S and Dqk = Dv = D, arguments in the order
  *   q, k, v, o, dout, lse, dq, dk, dv, B, S, Hq, Hkv, D, scale, causal, window, topk_idx,
  * followed by what the plain list cannot carry: topk, dtype, workspace, workspace_bytes, stream.

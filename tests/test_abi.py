@@ -200,3 +200,24 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 4, 1, 128, dtype=torch.float16)
     with pytest.raises(TypeError):
         ab.make_args(q, q, q, q, q, torch.zeros(1, 1, 4), q, q, q, scale=0.1)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1),
+    (dict(Hq=32, Hkv=5), -1),
+    (dict(Dqk=96, Dv=96), -2),
+    # more workspace than the static scratch: refused before any HIP call
+    (dict(B=8, Sq=65536, Skv=65536, Hq=32, Hkv=32), -3),
+])
+def test_noalloc_entry_point_validates_on_the_host(kw, status):
+    a = valid_args(**kw)
+    if status == -3:
+        assert ab.attn_bwd_workspace_size(a) > ab._lib.NOALLOC_SCRATCH_BYTES
+    rc = ab.load().attn_bwd_noalloc(ctypes.byref(a))
+    assert rc == status, (kw, rc, ab.attn_bwd_strerror(rc))
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ab._lib.NOALLOC_SCRATCH_BYTES
