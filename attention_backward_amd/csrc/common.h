@@ -204,6 +204,20 @@ __device__ __forceinline__ void b2lds4(i4v r, uint32_t voff, void *lds_base) {
                : "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base))), "v"(voff), "s"(r)
                : "memory", "m0");
 }
+// The same copies to an LDS byte address the caller computed once (no pointer conversion per
+// copy); `voff` is the lane's byte offset from the resource base.
+__device__ __forceinline__ void b2lds16_at(i4v r, uint32_t voff, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void b2lds4_at(i4v r, uint32_t voff, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
 // Wait for every outstanding vector-memory operation (vmcnt = 0; expcnt and lgkmcnt left at their
 // no-wait maxima in the gfx9 encoding).  Issued through the builtin so that the compiler's own
 // wait placement knows the loads it issued itself are complete from here on.

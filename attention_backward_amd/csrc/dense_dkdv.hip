@@ -136,27 +136,34 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
   const int qb_hi = q_hi > q_lo ? (q_hi + BN - 1) / BN : qb_lo;
   const int nsteps = (qb_hi - qb_lo) * Gs;
 
-  // Direct global->LDS loads of step t's Q/dO tile (rows past Sq are clamped to the last row;
-  // the mask zeroes them) and of its lse/delta rows.
+  // Direct global->LDS loads of step t's Q/dO tile and of its lse/delta rows, through buffer
+  // resources that start at the step's first row and head and end with the sequence: rows past
+  // Sq read as zero (the mask zeroes their scores).  The lanes' byte offsets within a tile are
+  // computed once; a step only forms its resources (scalar work).
+  uint32_t ld_off[C::WIW];
+#pragma unroll
+  for (int u = 0; u < C::WIW; u++) {
+    const int s = (w * C::WIW + u) * 64 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz<D>(row);
+    ld_off[u] = (uint32_t)((row * p.Hq * D + 8 * ch) * 2);
+  }
+  const uint32_t q_lds = lds_addr(&q_s[0][0]), do_lds = lds_addr(&do_s[0][0]);
+  const uint32_t row_lds = lds_addr(w == 0 ? &lse_s[0][0] : &dl_s[0][0]);
   auto issue = [&](int t, int qbuf, int buf) {
     const int q0 = (qb_lo + t / Gs) * BN;
     const int h = h0 + t % Gs;
+    const int64_t e0 = ((sv.q0 + q0) * p.Hq + h) * D;  // element (row q0, head h)
+    const uint64_t nbytes = ((uint64_t)(Sq - q0) * p.Hq - h) * D * 2;
+    const i4v rq = buf_rsrc(p.q + e0, nbytes), rd = buf_rsrc(p.dout + e0, nbytes);
 #pragma unroll
     for (int u = 0; u < C::WIW; u++) {
-      const int slot0 = (w * C::WIW + u) * 64;
-      const int s = slot0 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz<D>(row);
-      const int qi = min(q0 + row, Sq - 1);
-      const int64_t o64 = ((sv.q0 + qi) * p.Hq + h) * D + 8 * ch;
-      g2lds16(p.q + o64, &q_s[qbuf][slot0 * 8]);
-      g2lds16(p.dout + o64, &do_s[buf][slot0 * 8]);
+      const uint32_t slot_b = 16 * (w * C::WIW + u) * 64;
+      b2lds16_at(rq, ld_off[u], q_lds + 2 * qbuf * BN * D + slot_b);
+      b2lds16_at(rd, ld_off[u], do_lds + 2 * buf * BN * D + slot_b);
     }
     if (w < 2) {
-      const int qi = min(q0 + min(lane, BN - 1), Sq - 1);
-      const int64_t li = sv.l0 + (int64_t)h * p.Sq + qi;
-      if (w == 0)
-        g2lds4(p.lse + li, &lse_s[buf][0]);
-      else
-        g2lds4(p.ndelta + li, &dl_s[buf][0]);
+      const int64_t li = sv.l0 + (int64_t)h * p.Sq + q0;
+      const i4v rl = buf_rsrc((w == 0 ? p.lse : p.ndelta) + li, (uint64_t)(Sq - q0) * 4);
+      b2lds4_at(rl, (uint32_t)min(lane, BN - 1) * 4, row_lds + 4 * 64 * buf);
     }
   };
 

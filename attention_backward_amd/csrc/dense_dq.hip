@@ -128,24 +128,27 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   const int wlast = min(qw0 + 32, Sq) - 1;  // last valid query row of this wave
 
   // Direct global->LDS tile loads: slot s of a tile is physical chunk s % CPR of row s / CPR and
-  // holds logical chunk (s % CPR) ^ swz<D>(row).  Rows past the end are clamped to the last key
-  // (their scores are masked).
-  constexpr int NPART = 2 * C::WIW;
-  auto issue_part = [&](int t, int buf, int part) {
-    const int k0 = (kb_lo + t) * BK;
-    const int u = part >> 1;
-    const int slot0 = (w * C::WIW + u) * 64;
-    const int s = slot0 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz<D>(row);
-    const int kj = min(k0 + row, Skv - 1);
-    const int64_t o64 = ((sv.k0 + kj) * p.Hkv + g) * D + 8 * ch;
-    if (part & 1)
-      g2lds16(p.v + o64, &kv_s[buf][1][slot0 * 8]);
-    else
-      g2lds16(p.k + o64, &kv_s[buf][0][slot0 * 8]);
-  };
-  auto issue = [&](int t, int buf) {
+  // holds logical chunk (s % CPR) ^ swz<D>(row).  The loads go through buffer resources that start
+  // at the step's first key and end with the sequence, so key rows past the end read as zero
+  // (their scores are masked); the lanes' byte offsets within a tile are computed once.
+  uint32_t ld_off[C::WIW];
 #pragma unroll
-    for (int part = 0; part < NPART; part++) issue_part(t, buf, part);
+  for (int u = 0; u < C::WIW; u++) {
+    const int s = (w * C::WIW + u) * 64 + lane, row = s / C::CPR, ch = (s % C::CPR) ^ swz<D>(row);
+    ld_off[u] = (uint32_t)((row * p.Hkv * D + 8 * ch) * 2);
+  }
+  const uint32_t kv_lds = lds_addr(&kv_s[0][0][0]);
+  auto issue = [&](int t, int buf) {
+    const int k0 = (kb_lo + t) * BK;
+    const int64_t e0 = ((sv.k0 + k0) * p.Hkv + g) * D;  // element (key k0, KV head g)
+    const uint64_t nbytes = ((uint64_t)(Skv - k0) * p.Hkv - g) * D * 2;
+    const i4v rk = buf_rsrc(p.k + e0, nbytes), rv = buf_rsrc(p.v + e0, nbytes);
+#pragma unroll
+    for (int u = 0; u < C::WIW; u++) {
+      const uint32_t slot_b = 16 * (w * C::WIW + u) * 64;
+      b2lds16_at(rk, ld_off[u], kv_lds + 2 * (2 * buf + 0) * BK * D + slot_b);
+      b2lds16_at(rv, ld_off[u], kv_lds + 2 * (2 * buf + 1) * BK * D + slot_b);
+    }
   };
 
   // Per-lane LDS offsets (elements): natural read of key row 32*kb + lo, logical chunk
