@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libattn_bwd.so")
 
 ATTN_DT_F16, ATTN_DT_BF16 = 0, 1
 ATTN_OK, ATTN_E_INVAL, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = 0, -1, -2, -3, -4
+ATTN_BF16_AUTO, ATTN_BF16_SPLIT, ATTN_BF16_FP16 = 0, 1, 2
 _DT = {torch.float16: ATTN_DT_F16, torch.bfloat16: ATTN_DT_BF16}
 
 EXPORTS = ("attn_bwd", "attn_bwd_ex", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_bwd_delta", "attn_fwd",
@@ -39,6 +40,7 @@ class attn_bwd_args(ctypes.Structure):  # noqa: N801  (mirrors the C struct name
         ("events", ctypes.c_void_p),
         ("kv_shared", ctypes.c_int32),
         ("cu_seqlens", ctypes.c_void_p), ("nseq", ctypes.c_int64), ("max_seqlen", ctypes.c_int64),
+        ("bf16_arith", ctypes.c_int32),
     ]
 
 
@@ -110,7 +112,8 @@ def _stream(stream):
 
 
 def make_args(q, k, v, o, dout, lse, dq, dk, dv, *, scale, causal=True, window=0, topk_idx=None,
-              workspace=None, stream=None, kv_shared=False, cu_seqlens=None, max_seqlen=None) -> attn_bwd_args:
+              workspace=None, stream=None, kv_shared=False, cu_seqlens=None, max_seqlen=None,
+              bf16_arith=ATTN_BF16_AUTO) -> attn_bwd_args:
     """Fill an attn_bwd_args from torch tensors (shapes taken from q [B,Sq,Hq,Dqk], k and dout).
 
     kv_shared: the shared-latent form of the top-k path; v and dv are None, V is the first Dv
@@ -147,6 +150,7 @@ def make_args(q, k, v, o, dout, lse, dq, dk, dv, *, scale, causal=True, window=0
     a.causal = int(bool(causal))
     a.window = int(window)
     a.dtype = _DT[dt]
+    a.bf16_arith = int(bf16_arith)
     if workspace is not None:
         a.workspace = _dev(workspace, "workspace")
         a.workspace_bytes = workspace.numel() * workspace.element_size()

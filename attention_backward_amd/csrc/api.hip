@@ -50,6 +50,7 @@ int validate_sizes(const attn_bwd_args *a) {
   if (!(a->scale > 0.f) || !isfinite(a->scale)) return ATTN_E_INVAL;
   if (a->dtype != ATTN_DT_F16 && a->dtype != ATTN_DT_BF16) return ATTN_E_INVAL;
   if (a->kv_shared != 0 && a->kv_shared != 1) return ATTN_E_INVAL;
+  if (a->bf16_arith < ATTN_BF16_AUTO || a->bf16_arith > ATTN_BF16_FP16) return ATTN_E_INVAL;
   if (a->kv_shared && !a->topk_idx) return ATTN_E_UNSUPPORTED;  // the dense kernels have no shared form
   if (a->cu_seqlens) {
     // Packed sequences: a batch of one on the dense path, each sequence its own problem.
@@ -103,8 +104,24 @@ size_t queue_bytes(const attn_bwd_args *a) {
   if (!dkdv_queue(a)) return 0;
   return 256 + (dkdv_hsplit(a) > 1 ? 2 * part_bytes(a) : 0);
 }
+// bf16 calls re-expressed in fp16 (f16_prepass.hip): a 256-byte block (largest magnitudes, scales
+// and the factors that undo them) and scaled fp16 copies of q, k, v (none in the shared-latent
+// form, where V is part of K's rows), o and dout.  Automatic choice: from 2^22 elements of q up
+// (the copies cost about three passes over the inputs; the hi + lo products cost more there).
+bool f16x(const attn_bwd_args *a) {
+  if (a->dtype != ATTN_DT_BF16) return false;
+  if (a->bf16_arith == ATTN_BF16_FP16) return true;
+  return a->bf16_arith == ATTN_BF16_AUTO && a->B * a->Sq * a->Hq * a->Dqk >= ((int64_t)1 << 22);
+}
+size_t f16x_bytes(const attn_bwd_args *a) {
+  if (!f16x(a)) return 0;
+  const size_t nq = (size_t)(a->B * a->Sq * a->Hq), nk = (size_t)(a->B * a->Skv * a->Hkv);
+  size_t n = 256 + align256(nq * a->Dqk * 2) + align256(nk * a->Dqk * 2) + 2 * align256(nq * a->Dv * 2);
+  if (!a->kv_shared) n += align256(nk * a->Dv * 2);
+  return n;
+}
 size_t workspace_bytes_for(const attn_bwd_args *a) {
-  size_t n = 2 * row_stat_bytes(a);
+  size_t n = 2 * row_stat_bytes(a) + f16x_bytes(a);
   if (a->topk_idx) n += dk_acc_bytes(a) + dv_acc_bytes(a) + cnt_bytes(a);
   return n + queue_bytes(a);
 }
@@ -164,6 +181,9 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
   const bool shared = a->kv_shared != 0;
   hipStream_t st = (hipStream_t)a->stream;
   const bool bf16 = a->dtype == ATTN_DT_BF16;
+  const int arith = !bf16 ? attn::ARITH_F16 : f16x(a) ? attn::ARITH_F16B : attn::ARITH_BF16;
+  // The re-expressed inputs sit at the end of the workspace.
+  char *fx = (char *)ws + workspace_bytes_for(a) - f16x_bytes(a);
 
   attn::Params p;
   p.q = (const short *)a->q;
@@ -200,9 +220,39 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
 
   hipEvent_t *ev = (hipEvent_t *)a->events;
   hipError_t e = ev ? hipEventRecord(ev[0], st) : hipSuccess;
+  if (arith == attn::ARITH_F16B) {
+    // Scaled fp16 copies of the inputs; the kernels then read them and the factors in `rescale`.
+    unsigned *maxbits = (unsigned *)fx;
+    float *scales = (float *)(fx + 16), *rescale = (float *)(fx + 32);
+    const size_t nq = (size_t)(a->B * a->Sq * a->Hq), nk = (size_t)(a->B * a->Skv * a->Hkv);
+    char *cur = fx + 256;
+    auto take = [&](size_t elems) {
+      short *r = (short *)cur;
+      cur += align256(elems * 2);
+      return r;
+    };
+    short *q16 = take(nq * a->Dqk), *k16 = take(nk * a->Dqk);
+    short *v16 = shared ? k16 : take(nk * a->Dv);
+    short *o16 = take(nq * a->Dv), *do16 = take(nq * a->Dv);
+    attn::F16Copy cp[5];
+    int ncp = 0;
+    cp[ncp++] = attn::F16Copy{p.q, q16, (int64_t)(nq * a->Dqk), 0};
+    cp[ncp++] = attn::F16Copy{p.k, k16, (int64_t)(nk * a->Dqk), 1};
+    if (!shared) cp[ncp++] = attn::F16Copy{p.v, v16, (int64_t)(nk * a->Dv), 2};
+    cp[ncp++] = attn::F16Copy{p.o, o16, (int64_t)(nq * a->Dv), shared ? 1 : 2};  // O carries V's scale
+    cp[ncp++] = attn::F16Copy{p.dout, do16, (int64_t)(nq * a->Dv), 3};
+    if (e == hipSuccess) e = attn::launch_zero((float *)fx, 64, st);
+    if (e == hipSuccess) e = attn::launch_f16_prepass(cp, ncp, maxbits, scales, rescale, p.c, p.scale, st);
+    p.q = q16;
+    p.k = k16;
+    p.v = v16;
+    p.o = o16;
+    p.dout = do16;
+    p.rescale = rescale;
+  }
   if (!a->topk_idx) {
     // The dQ kernel forms delta and the lse copy in its prologue, so it runs first.
-    if (e == hipSuccess) e = attn::launch_dense_dq(p, bf16, st);
+    if (e == hipSuccess) e = attn::launch_dense_dq(p, arith, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
     if (dkdv_queue(a)) {
       char *qb = (char *)ws + 2 * row_stat_bytes(a);
@@ -216,13 +266,14 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
       // Only the counter starts at zero: every slice row inside a sequence is stored by its item.
       if (e == hipSuccess) e = attn::launch_zero((float *)p.work, 64, st);
     }
-    if (e == hipSuccess) e = attn::launch_dense_dkdv(p, bf16, st);
+    if (e == hipSuccess) e = attn::launch_dense_dkdv(p, arith, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
-    if (p.hsplit > 1 && e == hipSuccess) e = attn::launch_land_parts(p, bf16, st);
+    if (p.hsplit > 1 && e == hipSuccess) e = attn::launch_land_parts(p, arith, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
   } else {
     if (e == hipSuccess)
-      e = attn::launch_delta(p.o, p.dout, p.ndelta, a->lse, (float *)p.lse, true, a->B, a->Sq, a->Hq, a->Dv, bf16, st);
+      e = attn::launch_delta(p.o, p.dout, p.ndelta, a->lse, (float *)p.lse, true, a->B, a->Sq, a->Hq, a->Dv,
+                             arith == attn::ARITH_BF16, st);
     float *dk_acc = (float *)((char *)ws + 2 * row_stat_bytes(a));
     float *dv_acc = (float *)((char *)dk_acc + dk_acc_bytes(a));
     uint16_t *cnt = (uint16_t *)((char *)dv_acc + dv_acc_bytes(a));
@@ -232,16 +283,17 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
     if (e == hipSuccess)
       e = attn::launch_topk_count(a->topk_idx, cnt, a->B, a->Sq, a->Skv, a->Hkv, a->topk, (int)skv_pad(a), a->causal,
                                   st);
-    if (e == hipSuccess) e = attn::launch_sparse_dq(p, bf16, st);
+    if (e == hipSuccess) e = attn::launch_sparse_dq(p, arith, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-    if (e == hipSuccess) e = attn::launch_sparse_dkdv(p, cnt, (int)skv_pad(a), dk_acc, dv_acc, bf16, st);
+    if (e == hipSuccess) e = attn::launch_sparse_dkdv(p, cnt, (int)skv_pad(a), dk_acc, dv_acc, arith, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
     if (shared) {
       if (e == hipSuccess)
-        e = attn::launch_land_kv(dk_acc, dv_acc, p.dk, a->B * a->Skv * a->Hkv, a->Dqk, a->Dv, a->scale, bf16, st);
+        e = attn::launch_land_kv(dk_acc, dv_acc, p.dk, a->B * a->Skv * a->Hkv, a->Dqk, a->Dv, a->scale, p.rescale, bf16,
+                                 st);
     } else {
-      if (e == hipSuccess) e = attn::launch_land(dk_acc, p.dk, nk, a->scale, bf16, st);
-      if (e == hipSuccess) e = attn::launch_land(dv_acc, p.dv, nv, 1.0f, bf16, st);
+      if (e == hipSuccess) e = attn::launch_land(dk_acc, p.dk, nk, a->scale, p.rescale, 2, bf16, st);
+      if (e == hipSuccess) e = attn::launch_land(dv_acc, p.dv, nv, 1.0f, p.rescale, 3, bf16, st);
     }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
   }

@@ -48,6 +48,11 @@ struct Params {
   float *dv_acc = nullptr;            //   part (plain stores; the landing pass adds them)
   int64_t acc_slice = 0;              // elements per slice (tokens * Hkv * D)
   int *work = nullptr;                // dK/dV work-queue counter (zeroed), or null
+  // bf16 calls computed in fp16: the inputs are fp16 copies scaled by powers of two, and the
+  // factors that undo those scales live in device memory: [0] the exponent scale c, [1] the dQ
+  // output factor, [2] the dK factor, [3] the dV factor, [4] the factor that brings dS back to its
+  // own scale before its fp16 rounding (null: c and scale above, dV factor 1).
+  const float *rescale = nullptr;
 };
 
 // The sequence one workgroup works on.  Dense: batch s of equal-length sequences.  Packed (cu not
@@ -84,15 +89,18 @@ __device__ __forceinline__ SeqView seq_view(const int32_t *cu, int s, int Sq_tot
 // need no split.
 struct F16 {
   static constexpr bool SPLIT = false;
+  static constexpr bool RESCALED = false;  // inputs are scaled copies (Factors::ds applies)
   static __device__ __forceinline__ f16v mfma(s8v a, s8v b, f16v c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8v, a), __builtin_bit_cast(h8v, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ short cvt(float x) { return __builtin_bit_cast(short, (_Float16)x); }
   static __device__ __forceinline__ float tof(short x) { return (float)__builtin_bit_cast(_Float16, x); }
+  static __device__ __forceinline__ short cvt_out(float x) { return cvt(x); }  // dq, dk, dv
 };
 
 struct BF16 {
   static constexpr bool SPLIT = true;
+  static constexpr bool RESCALED = false;
   static __device__ __forceinline__ f16v mfma(s8v a, s8v b, f16v c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8v, a), __builtin_bit_cast(b8v, b), c, 0, 0, 0);
   }
@@ -100,7 +108,30 @@ struct BF16 {
   static __device__ __forceinline__ float tof(short x) {
     return __builtin_bit_cast(float, ((unsigned)(unsigned short)x) << 16);
   }
+  static __device__ __forceinline__ short cvt_out(float x) { return cvt(x); }
 };
+
+// bf16 calls re-expressed in fp16: operands and products in fp16 (no hi + lo split: P and dS are
+// rounded once to fp16's 11 bits, as on the fp16 path), outputs rounded to bf16.
+struct F16B : F16 {
+  static constexpr bool RESCALED = true;
+  static __device__ __forceinline__ short cvt_out(float x) { return BF16::cvt(x); }
+};
+
+// The exponent scale c and the output factors of a call: from device memory when the inputs were
+// re-expressed, else c, scale (dQ and dK) and 1 (dV).
+struct Factors {
+  float c, dq, dk, dv, ds;
+};
+__device__ __forceinline__ Factors factors(const Params &p) {
+  if (p.rescale) return Factors{p.rescale[0], p.rescale[1], p.rescale[2], p.rescale[3], p.rescale[4]};
+  return Factors{p.c, p.scale, p.scale, 1.f, 1.f};
+}
+// dS = P (dP - delta) in its own scale: with rescaled inputs the difference carries s_do s_v.
+template <class TT>
+__device__ __forceinline__ float ds_of(float p, float dp_minus_delta, const Factors &f) {
+  return TT::RESCALED ? p * dp_minus_delta * f.ds : p * dp_minus_delta;
+}
 
 __device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 

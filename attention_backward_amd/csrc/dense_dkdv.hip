@@ -252,6 +252,7 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
       s[mb] = TT::mfma(ring[n % (PF + 1)], kv[kk], s[mb]);
     }
   };
+  const Factors fac = factors(p);
   auto step_q0 = [&](int t) { return (qb_lo + t / Gs) * BN; };
   auto step_full = [&](int q0) {
     return (!p.causal || k0 + C::BM - 1 <= q0 + off) && (p.window <= 0 || k0 > q0 + BN - 1 + off - p.window) &&
@@ -281,7 +282,7 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
             f4v pq;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-              float x = exp2f_hw(s[mb][4 * j + i] * p.c - l4[i]);
+              float x = exp2f_hw(s[mb][4 * j + i] * fac.c - l4[i]);
               if (decltype(masked)::value) {
                 const int qi = q0 + 32 * mb + 8 * j + 4 * hi + i;
                 x = ((qi >= qlo) & (qi <= qhi)) ? x : 0.f;
@@ -332,11 +333,11 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
           if (PH) {
             const s8v ph = ph_s[kgrp][2 * mb + (j >> 1)][lane];
 #pragma unroll
-            for (int i = 0; i < 4; i++) pack(da, dl, mb, 4 * j + i, TT::tof(ph[4 * (j & 1) + i]) * s[mb][4 * j + i]);
+            for (int i = 0; i < 4; i++) pack(da, dl, mb, 4 * j + i, ds_of<TT>(TT::tof(ph[4 * (j & 1) + i]), s[mb][4 * j + i], fac));
           } else {
             const f4v pq = p_s[kgrp][mb][j][lane];
 #pragma unroll
-            for (int i = 0; i < 4; i++) pack(da, dl, mb, 4 * j + i, pq[i] * s[mb][4 * j + i]);
+            for (int i = 0; i < 4; i++) pack(da, dl, mb, 4 * j + i, ds_of<TT>(pq[i], s[mb][4 * j + i], fac));
           }
         }
       wait_vm0();
@@ -346,7 +347,7 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
   }
 
   // Epilogue: dV (P role) or scale * dK (dS role), cast once, BSHD at the KV head.
-  const float sc = role == 0 ? 1.f : p.scale;
+  const float sc = role == 0 ? fac.dv : fac.dk;
   if (p.hsplit > 1) {
     // Part sp of the head group stores its unscaled f32 block with plain stores into its own
     // slice [sp][tokens, Hkv, D]; the landing pass adds the slices in a fixed order.
@@ -369,7 +370,7 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
     if (key < Skv) {
       short *row = dst + ((sv.k0 + key) * p.Hkv + g) * D + lo;
 #pragma unroll
-      for (int dn = 0; dn < C::ND; dn++) row[32 * dn] = TT::cvt(acc[dn][r] * sc);
+      for (int dn = 0; dn < C::ND; dn++) row[32 * dn] = TT::cvt_out(acc[dn][r] * sc);
     }
   }
 }
@@ -433,35 +434,45 @@ __global__ __launch_bounds__(256) void land_parts_kernel(const Params p, int64_t
 #pragma unroll
   for (int t = 0; t < 2; t++) {
     const float *a0 = acc[t] + e, *a1 = acc[t] + p.acc_slice + e;
-    const float sc = t == 0 ? p.scale : 1.f;
+    const Factors fac = factors(p);
+    const float sc = t == 0 ? fac.dk : fac.dv;
     const f4v x0 = *(const f4v *)a0 + *(const f4v *)a1;
     const f4v x1 = *(const f4v *)(a0 + 4) + *(const f4v *)(a1 + 4);
     s8v o;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      o[i] = TT::cvt(x0[i] * sc);
-      o[4 + i] = TT::cvt(x1[i] * sc);
+      o[i] = TT::cvt_out(x0[i] * sc);
+      o[4 + i] = TT::cvt_out(x1[i] * sc);
     }
     *(s8v *)(out[t] + e) = o;
   }
 }
 
-hipError_t launch_land_parts(const Params &p, bool bf16, hipStream_t st) {
+hipError_t launch_land_parts(const Params &p, int arith, hipStream_t st) {
+  const bool bf16 = arith != ARITH_F16;  // the storage dtype decides the output cast
   if (!p.cu || p.hsplit != 2 || (p.Hkv * p.Dqk) % 8 != 0) return hipErrorInvalidValue;
   const int64_t bps = ((int64_t)p.max_seqlen * p.Hkv * p.Dqk / 8 + 255) / 256;
   const int64_t blocks = bps * p.nseq;
   if (blocks < 1) return hipSuccess;
   if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  if (bf16)
+  if (arith == ARITH_F16B)
+    hipLaunchKernelGGL(land_parts_kernel<F16B>, dim3((unsigned)blocks), dim3(256), 0, st, p, bps);
+  else if (bf16)
     hipLaunchKernelGGL(land_parts_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, p, bps);
   else
     hipLaunchKernelGGL(land_parts_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, p, bps);
   return hipGetLastError();
 }
 
-hipError_t launch_dense_dkdv(const Params &p, bool bf16, hipStream_t st) {
-  if (p.Dqk == 128) return bf16 ? launch_dkdv_t<BF16, 128, 64>(p, st) : launch_dkdv_t<F16, 128, 64>(p, st);
-  if (p.Dqk == 64) return bf16 ? launch_dkdv_t<BF16, 64, 64>(p, st) : launch_dkdv_t<F16, 64, 64>(p, st);
+hipError_t launch_dense_dkdv(const Params &p, int arith, hipStream_t st) {
+  if (p.Dqk == 128)
+    return arith == ARITH_BF16 ? launch_dkdv_t<BF16, 128, 64>(p, st)
+           : arith == ARITH_F16B ? launch_dkdv_t<F16B, 128, 64>(p, st)
+                                 : launch_dkdv_t<F16, 128, 64>(p, st);
+  if (p.Dqk == 64)
+    return arith == ARITH_BF16 ? launch_dkdv_t<BF16, 64, 64>(p, st)
+           : arith == ARITH_F16B ? launch_dkdv_t<F16B, 64, 64>(p, st)
+                                 : launch_dkdv_t<F16, 64, 64>(p, st);
   return hipErrorInvalidValue;
 }
 

@@ -113,6 +113,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
   const int klo = p.window > 0 ? qi + off - p.window + 1 : 0;
   const int khi = !qok ? klo - 1 : p.causal ? min(qi + off, Skv - 1) : Skv - 1;
 
+  const Factors fac = factors(p);
   f16v acc[C::ND];  // dQ rows of this wave's 32 queries, [32-wide d block]
 #pragma unroll
   for (int dn = 0; dn < C::ND; dn++) acc[dn] = f16v{};
@@ -238,12 +239,12 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
           for (int kb = 0; kb < KBS; kb++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-              float x = exp2f_hw(s[kb][r] * p.c - lr);
+              float x = exp2f_hw(s[kb][r] * fac.c - lr);
               if (decltype(masked)::value) {
                 const int kj = k0 + 32 * (sb * KBS + kb) + 8 * (r >> 2) + 4 * hi + (r & 3);
                 x = ((kj >= klo) & (kj <= khi)) ? x : 0.f;
               }
-              const float ds = x * dp[kb][r];
+              const float ds = ds_of<TT>(x, dp[kb][r], fac);
               const short dh = TT::cvt(ds);
               da[2 * kb + (r >> 3)][r & 7] = dh;
               dl[2 * kb + (r >> 3)][r & 7] = TT::SPLIT ? TT::cvt(ds - TT::tof(dh)) : (short)0;
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
     if (qr < Sq) {
       short *row = p.dq + ((sv.q0 + qr) * p.Hq + h) * D + lo;
 #pragma unroll
-      for (int dn = 0; dn < C::ND; dn++) row[32 * dn] = TT::cvt(acc[dn][r] * p.scale);
+      for (int dn = 0; dn < C::ND; dn++) row[32 * dn] = TT::cvt_out(acc[dn][r] * fac.dq);
     }
   }
 }
@@ -313,12 +314,18 @@ static hipError_t launch_dq_t(const Params &p, hipStream_t st) {
 #define ATTN_DQ128_SB 2
 #endif
 
-hipError_t launch_dense_dq(const Params &p, bool bf16, hipStream_t st) {
+hipError_t launch_dense_dq(const Params &p, int arith, hipStream_t st) {
   // At D = 128, 64-key tiles are taken as two 32-key sub-blocks, so that the S/dP accumulators of
   // one sub-block (and, for bf16, dS as hi + lo halves) fit in 256 VGPRs without spilling.
   constexpr int BK = ATTN_DQ128_BK, SB = ATTN_DQ128_SB;
-  if (p.Dqk == 128) return bf16 ? launch_dq_t<BF16, 128, BK, SB>(p, st) : launch_dq_t<F16, 128, BK, SB>(p, st);
-  if (p.Dqk == 64) return bf16 ? launch_dq_t<BF16, 64, 64, 1>(p, st) : launch_dq_t<F16, 64, 64, 1>(p, st);
+  if (p.Dqk == 128)
+    return arith == ARITH_BF16 ? launch_dq_t<BF16, 128, BK, SB>(p, st)
+           : arith == ARITH_F16B ? launch_dq_t<F16B, 128, BK, SB>(p, st)
+                                 : launch_dq_t<F16, 128, BK, SB>(p, st);
+  if (p.Dqk == 64)
+    return arith == ARITH_BF16 ? launch_dq_t<BF16, 64, 64, 1>(p, st)
+           : arith == ARITH_F16B ? launch_dq_t<F16B, 64, 64, 1>(p, st)
+                                 : launch_dq_t<F16, 64, 64, 1>(p, st);
   return hipErrorInvalidValue;
 }
 

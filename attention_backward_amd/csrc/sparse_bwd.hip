@@ -73,6 +73,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
   // Workgroups of the same (query row, KV head) gather the same K/V rows: the nhb head blocks of
   // one query are placed 8 apart in the dispatch order, which the hardware hands to the same XCD
   // at about the same time, so most second gathers of a row hit that XCD's L2.
+  const Factors fac = factors(p);
   const int nhb = (p.G + C::HB - 1) / C::HB;
   int x = blockIdx.x;
   int hb;
@@ -245,8 +246,8 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
         const float sv = part_s[0][r][lane] + part_s[1][r][lane];
         const float dpv = part_s[2][r][lane] + part_s[3][r][lane];
         const bool ok = slot_ok && m < nh;
-        const float pr = exp2f_hw(sv * p.c - lse_r[r]);
-        const float ds = ok ? pr * (dpv + dl_r[r]) : 0.f;
+        const float pr = exp2f_hw(sv * fac.c - lse_r[r]);
+        const float ds = ok ? ds_of<TT>(pr, dpv + dl_r[r], fac) : 0.f;
         const short dh = TT::cvt(ds);
         st_ds[0][m * C::KC + lo] = dh;
         if (TT::SPLIT) st_ds[1][m * C::KC + lo] = TT::cvt(ds - TT::tof(dh));
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int m = 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (m < nh) p.dq[(qrow + h0 + m) * DQK + 32 * nb + lo] = TT::cvt(dq[u][r] * p.scale);
+        if (m < nh) p.dq[(qrow + h0 + m) * DQK + 32 * nb + lo] = TT::cvt_out(dq[u][r] * fac.dq);
       }
     }
   }
@@ -306,7 +307,8 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
 // thread, 32-byte reads and 16-byte writes).
 template <class TT>
 __global__ __launch_bounds__(256) void land_kernel(const float *__restrict__ acc, short *__restrict__ out, int64_t n8,
-                                                   float scale) {
+                                                   float scale, const float *rescale, int which) {
+  if (rescale) scale = rescale[which];  // re-expressed bf16 call: the factor that undoes the scales
   for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n8; v += (int64_t)gridDim.x * 256) {
     const f4v a = *(const f4v *)&acc[8 * v];
     const f4v c = *(const f4v *)&acc[8 * v + 4];
@@ -325,7 +327,9 @@ __global__ __launch_bounds__(256) void land_kernel(const float *__restrict__ acc
 template <class TT>
 __global__ __launch_bounds__(256) void land_kv_kernel(const float *__restrict__ dk_acc, const float *__restrict__ dv_acc,
                                                       short *__restrict__ out, int64_t n8, int c8k, int c8v,
-                                                      float scale) {
+                                                      float scale, const float *rescale) {
+  const float sv = rescale ? rescale[3] : 1.f;
+  if (rescale) scale = rescale[2];
   for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n8; v += (int64_t)gridDim.x * 256) {
     const int64_t r = v / c8k;
     const int c = (int)(v - r * c8k);
@@ -333,8 +337,8 @@ __global__ __launch_bounds__(256) void land_kv_kernel(const float *__restrict__ 
     f4v b = *(const f4v *)&dk_acc[8 * v + 4] * scale;
     if (c < c8v) {
       const float *d = &dv_acc[8 * (r * c8v + c)];
-      a += *(const f4v *)d;
-      b += *(const f4v *)(d + 4);
+      a += *(const f4v *)d * sv;
+      b += *(const f4v *)(d + 4) * sv;
     }
     s8v o;
 #pragma unroll
@@ -360,32 +364,35 @@ hipError_t launch_zero(float *buf, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_dq(const Params &p, bool bf16, hipStream_t st) {
+hipError_t launch_sparse_dq(const Params &p, int arith, hipStream_t st) {
   if (p.Dqk != 576 || p.Dv != 512) return hipErrorInvalidValue;
   const int nhb = (p.G + SpCfg<576, 512>::HB - 1) / SpCfg<576, 512>::HB;
   const int64_t blocks = (int64_t)p.B * p.Sq * p.Hkv * nhb;
   if (blocks < 1) return hipSuccess;
-  if (bf16)
+  if (arith == ARITH_BF16)
     hipLaunchKernelGGL((sparse_dq_kernel<BF16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  else if (arith == ARITH_F16B)
+    hipLaunchKernelGGL((sparse_dq_kernel<F16B, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((sparse_dq_kernel<F16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_land(const float *acc, short *out, int64_t n, float scale, bool bf16, hipStream_t st) {
+hipError_t launch_land(const float *acc, short *out, int64_t n, float scale, const float *rescale, int which, bool bf16,
+                       hipStream_t st) {
   const int64_t n8 = n / 8;  // callers pass multiples of 8 elements
   int64_t blocks = (n8 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(land_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, acc, out, n8, scale);
+    hipLaunchKernelGGL(land_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, acc, out, n8, scale, rescale, which);
   else
-    hipLaunchKernelGGL(land_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, acc, out, n8, scale);
+    hipLaunchKernelGGL(land_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, acc, out, n8, scale, rescale, which);
   return hipGetLastError();
 }
 
 hipError_t launch_land_kv(const float *dk_acc, const float *dv_acc, short *out, int64_t rows, int64_t Dqk, int64_t Dv,
-                          float scale, bool bf16, hipStream_t st) {
+                          float scale, const float *rescale, bool bf16, hipStream_t st) {
   if (Dqk % 8 != 0 || Dv % 8 != 0 || Dv > Dqk) return hipErrorInvalidValue;
   const int64_t n8 = rows * (Dqk / 8);
   int64_t blocks = (n8 + 255) / 256;
@@ -393,10 +400,10 @@ hipError_t launch_land_kv(const float *dk_acc, const float *dv_acc, short *out, 
   if (blocks < 1) return hipSuccess;
   if (bf16)
     hipLaunchKernelGGL(land_kv_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, dk_acc, dv_acc, out, n8,
-                       (int)(Dqk / 8), (int)(Dv / 8), scale);
+                       (int)(Dqk / 8), (int)(Dv / 8), scale, rescale);
   else
     hipLaunchKernelGGL(land_kv_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, dk_acc, dv_acc, out, n8,
-                       (int)(Dqk / 8), (int)(Dv / 8), scale);
+                       (int)(Dqk / 8), (int)(Dv / 8), scale, rescale);
   return hipGetLastError();
 }
 

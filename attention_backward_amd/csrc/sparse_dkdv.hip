@@ -75,6 +75,10 @@ __device__ __forceinline__ f4v mfma16<F16>(s8v a, s8v b, f4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8v, a), __builtin_bit_cast(h8v, b), c, 0, 0, 0);
 }
 template <>
+__device__ __forceinline__ f4v mfma16<F16B>(s8v a, s8v b, f4v c) {
+  return mfma16<F16>(a, b, c);
+}
+template <>
 __device__ __forceinline__ f4v mfma16<BF16>(s8v a, s8v b, f4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8v, a), __builtin_bit_cast(b8v, b), c, 0, 0, 0);
 }
@@ -119,6 +123,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int j0 = kb * C::BM;
   const int off = p.Skv - p.Sq;
+  const Factors fac = factors(p);
   const int nhb = (p.G + C::HB - 1) / C::HB;
   // Query chunk qc, counted from the end: [max(i_lo, Sq - (qc+1)*qchunk), Sq - qc*qchunk).
   const int i_lo = p.causal ? max(0, j0 - off) : 0;
@@ -243,8 +248,8 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
       for (int r = 0; r < 4; r++) {
         const int key = 16 * kh + 4 * g16 + r;
         const float c = (float)cnt_s[buf][key];
-        const float pr = (hok && c > 0.f) ? c * exp2f_hw(sv[r] * p.c - l) : 0.f;
-        const float ds = pr * (dpv[r] + dl);  // dl = minus delta
+        const float pr = (hok && c > 0.f) ? c * exp2f_hw(sv[r] * fac.c - l) : 0.f;
+        const float ds = ds_of<TT>(pr, dpv[r] + dl, fac);  // dl = minus delta
         const short ph = TT::cvt(pr), dh = TT::cvt(ds);
         st_p[0][key * C::HB + head] = ph;
         st_ds[0][key * C::HB + head] = dh;
@@ -333,7 +338,7 @@ hipError_t launch_topk_count(const int32_t *idx, uint16_t *cnt, int64_t B, int64
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_dkdv(const Params &p, const uint16_t *cnt, int skv_pad, float *dk_acc, float *dv_acc, bool bf16,
+hipError_t launch_sparse_dkdv(const Params &p, const uint16_t *cnt, int skv_pad, float *dk_acc, float *dv_acc, int arith,
                               hipStream_t st) {
   if (p.Dqk != 576 || p.Dv != 512) return hipErrorInvalidValue;
   constexpr int BM = SkCfg<576, 512>::BM;
@@ -345,8 +350,11 @@ hipError_t launch_sparse_dkdv(const Params &p, const uint16_t *cnt, int skv_pad,
   const int nchunk = (p.Sq + qchunk - 1) / qchunk;
   const int64_t blocks = (int64_t)nchunk * nkb * p.B * p.Hkv;
   if (blocks < 1) return hipSuccess;
-  if (bf16)
+  if (arith == ARITH_BF16)
     hipLaunchKernelGGL((sparse_dkdv_kernel<BF16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p, cnt, skv_pad,
+                       qchunk, nchunk, dk_acc, dv_acc);
+  else if (arith == ARITH_F16B)  // rescaled inputs: dS is brought back to its own scale
+    hipLaunchKernelGGL((sparse_dkdv_kernel<F16B, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p, cnt, skv_pad,
                        qchunk, nchunk, dk_acc, dv_acc);
   else
     hipLaunchKernelGGL((sparse_dkdv_kernel<F16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p, cnt, skv_pad,

@@ -115,7 +115,19 @@ typedef struct {
   int64_t nseq;                     /* packed: number of sequences (>= 1); else 0              */
   int64_t max_seqlen;               /* packed: a bound on every sequence length, 1..T (sizes the
                                        grid; a longer sequence is cut there); else 0            */
+  int32_t bf16_arith;               /* bf16 calls only (ignored for fp16): ATTN_BF16_AUTO, or
+                                       ATTN_BF16_SPLIT: bf16 products, with P and dS entering
+                                       them as hi + lo bf16 halves; or ATTN_BF16_FP16: the inputs
+                                       are copied to fp16 with one power-of-two scale per tensor
+                                       (exact for values within 2^28 of the tensor's largest
+                                       magnitude, which lands just below 2^15), the fp16
+                                       kernels run on the copies, and dq, dk, dv come back in
+                                       bf16 with the scales undone.  AUTO takes FP16 from
+                                       B * Sq * Hq * Dqk >= 2^22 on.  FP16 adds scaled copies
+                                       of q, k, v, o and dout to the workspace.                  */
 } attn_bwd_args;
+
+enum { ATTN_BF16_AUTO = 0, ATTN_BF16_SPLIT = 1, ATTN_BF16_FP16 = 2 };
 
 /* Bytes of workspace the call needs for these sizes (0 if the arguments are invalid), as
  * 256-byte aligned parts:

@@ -93,6 +93,8 @@ def test_workspace_size():
         (dict(workspace=0x100000, workspace_bytes=16), -3),
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, kv_shared=2), -1),
         (dict(kv_shared=1), -2),  # the shared-latent form exists on the top-k path only
+        (dict(bf16_arith=3), -1),
+        (dict(bf16_arith=-1), -1),
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, kv_shared=1), -1),  # v and dv must be NULL
         # a valid shared-latent call up to the workspace check
         (dict(topk_idx=0x100000, topk=8, Dqk=576, Dv=512, kv_shared=1, v=0, dv=0, workspace=0x100000,
@@ -180,6 +182,25 @@ def test_forward_varlen_entry_point_validates(kw, status):
                                    a["T"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["window"],
                                    a["dtype"], None)
     assert rc == status
+
+
+def test_bf16_reexpression_workspace():
+    """bf16 calls computed on fp16 copies add a 256-byte block and the copies of q, k, v, o, dout;
+    the automatic choice takes that path from 2^22 elements of q on, fp16 calls never."""
+    rows = 2 * (2 * 32 * 2048 * 4)
+    nq, nk = 2 * 2048 * 32 * 128, 2 * 2048 * 8 * 128
+    copies = 256 + 2 * nq + 2 * nk + 2 * nk + 2 * (2 * nq)
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=8, dtype=1, bf16_arith=2)) == rows + copies
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=8, dtype=1, bf16_arith=0)) == rows + copies  # 2^24 elements
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=8, dtype=1, bf16_arith=1)) == rows
+    assert ab.attn_bwd_workspace_size(valid_args(Hkv=8, dtype=0, bf16_arith=2)) == rows
+    # below 2^22 elements of q the automatic choice keeps the bf16 products
+    small = valid_args(B=1, Sq=256, Skv=256, Hq=2, Hkv=2, dtype=1)
+    assert ab.attn_bwd_workspace_size(small) == 2 * align(2 * 256 * 4)
+
+
+def align(n):
+    return (n + 255) // 256 * 256
 
 
 def test_packed_workspace():

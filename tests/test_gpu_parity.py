@@ -21,11 +21,11 @@ pytestmark = pytest.mark.gpu
 W = synth.WORKLOADS
 
 
-def run(inp, w):
+def run(inp, w, bf16_arith=ab._lib.ATTN_BF16_AUTO):
     g = to_gpu(inp)
     dq, dk, dv = poisoned_like(g["q"]), poisoned_like(g["k"]), poisoned_like(g["v"])
     args = ab.make_args(g["q"], g["k"], g["v"], g["o"], g["dout"], g["lse"], dq, dk, dv, scale=w.scale,
-                        causal=w.causal, window=w.window, topk_idx=g["idx"])
+                        causal=w.causal, window=w.window, topk_idx=g["idx"], bf16_arith=bf16_arith)
     need = ab.attn_bwd_workspace_size(args)
     assert need > 0
     ws = poisoned_like(torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda"))
@@ -35,11 +35,11 @@ def run(inp, w):
     return dq.cpu(), dk.cpu(), dv.cpu()
 
 
-def full_compare(w, inp=None):
+def full_compare(w, inp=None, bf16_arith=ab._lib.ATTN_BF16_AUTO):
     log(f"case {w.name}: B={w.B} Sq={w.Sq} Skv={w.Skv} Hq={w.Hq} Hkv={w.Hkv} D={w.Dqk}/{w.Dv} {w.dtype} "
-        f"causal={w.causal} window={w.window} topk={w.topk}")
+        f"causal={w.causal} window={w.window} topk={w.topk} bf16_arith={bf16_arith}")
     inp = inp or prepare(w)
-    dq, dk, dv = run(inp, w)
+    dq, dk, dv = run(inp, w, bf16_arith)
     ref = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["o"], inp["dout"], inp["lse"], w.scale, w.causal, w.window,
                      inp["idx"])
     for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
@@ -73,6 +73,38 @@ SMALL = [
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_small_full_parity(w):
     full_compare(w)
+
+
+BF16_SMALL = [w for w in SMALL if w.dtype == "bf16"]
+
+
+@pytest.mark.parametrize("mode", ["split", "fp16"])
+@pytest.mark.parametrize("w", BF16_SMALL, ids=[w.name for w in BF16_SMALL])
+def test_small_bf16_both_arithmetics(w, mode):
+    """bf16 calls either keep bf16 products with hi + lo P and dS operands, or run the fp16 kernels
+    on fp16 copies of the inputs scaled by powers of two (bf16 outputs); both meet the tolerance."""
+    full_compare(w, bf16_arith=ab._lib.ATTN_BF16_SPLIT if mode == "split" else ab._lib.ATTN_BF16_FP16)
+
+
+def test_bf16_reexpression_scales_out_of_fp16_range():
+    """Inputs far outside fp16's range (|q| ~ 2^40, |k| ~ 2^-40, |dO| ~ 2^20, V and O ~ 2^-30) in
+    bf16: the power-of-two scales bring each tensor into range and the factors undo them."""
+    w = small("bf16_far_scales", Sq=200, Skv=200, Hq=4, Hkv=2, dtype="bf16", seed=130)
+    inp = synth.make_inputs(w)
+    s_q, s_k, s_v, s_do = 2.0 ** 40, 2.0 ** -40, 2.0 ** -30, 2.0 ** 20
+    inp["q"] = (inp["q"].double() * s_q).to(torch.bfloat16)
+    inp["k"] = (inp["k"].double() * s_k).to(torch.bfloat16)
+    inp["v"] = (inp["v"].double() * s_v).to(torch.bfloat16)
+    inp["dout"] = (inp["dout"].double() * s_do).to(torch.bfloat16)
+    from oracle import forward as oracle_forward
+    inp["o"], inp["lse"] = oracle_forward.make_o_lse(w, inp)
+    dq, dk, dv = run(inp, w, ab._lib.ATTN_BF16_FP16)
+    ref = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["o"], inp["dout"], inp["lse"], w.scale, w.causal, w.window)
+    # compare in the units of each output's own magnitude
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        m = float(np.abs(r).max())
+        assert m > 0 and np.isfinite(m)
+        check_close(name + " (relative to its largest magnitude)", got.double().numpy() / m, r / m)
 
 
 DET = [SMALL[1], SMALL[-2], SMALL[-1]]  # G = 4; G = 8 without a window, fp16 and bf16

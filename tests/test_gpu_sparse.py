@@ -40,6 +40,14 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("w", [w for w in SMALL if w.dtype == "bf16"], ids=lambda w: w.name)
+def test_sparse_small_bf16_reexpressed_in_fp16(w):
+    """The top-k kernels on fp16 copies of bf16 inputs scaled by powers of two (bf16 outputs)."""
+    from attention_backward_amd import _lib
+
+    full_compare(w, bf16_arith=_lib.ATTN_BF16_FP16)
+
+
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_sparse_small_full_parity(w):
     inp = prepare(w)

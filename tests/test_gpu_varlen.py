@@ -53,12 +53,12 @@ def gpu_fwd(inp, w):
     return o.cpu(), lse.cpu()
 
 
-def gpu_bwd(inp, o, lse, w):
+def gpu_bwd(inp, o, lse, w, bf16_arith=0):
     g = {n: inp[n].cuda() for n in ("q", "k", "v", "dout", "cu")}
     o, lse = o.cuda(), lse.cuda()
     dq, dk, dv = poisoned_like(g["q"]), poisoned_like(g["k"]), poisoned_like(g["v"])
     args = ab.make_args(g["q"], g["k"], g["v"], o, g["dout"], lse, dq, dk, dv, scale=w.scale, causal=w.causal,
-                        window=w.window, cu_seqlens=g["cu"], max_seqlen=inp["max_seqlen"])
+                        window=w.window, cu_seqlens=g["cu"], max_seqlen=inp["max_seqlen"], bf16_arith=bf16_arith)
     need = ab.attn_bwd_workspace_size(args)
     assert need > 0
     ws = poisoned_like(torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda"))
@@ -78,6 +78,18 @@ def test_varlen_small_full_parity(w):
     check_close("o", o.double().numpy(), ref_o)
     check_lse("lse", lse.numpy(), ref_lse)
     dq, dk, dv = gpu_bwd(inp, o_st, lse32, w)
+    ref = oracle.bwd_varlen(inp["q"], inp["k"], inp["v"], o_st, inp["dout"], lse32, inp["cu"], w.scale, w.causal,
+                            w.window)
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        check_close(name, got.double().numpy(), r)
+
+
+@pytest.mark.parametrize("w", [w for w in SMALL if w.dtype == "bf16"], ids=lambda w: w.name)
+def test_varlen_bf16_reexpressed_in_fp16(w):
+    """Packed bf16 sequences through the fp16 kernels on scaled fp16 copies (bf16 outputs)."""
+    inp = synth.make_varlen_inputs(w)
+    _, _, o_st, lse32 = oracle_o_lse(inp, w)
+    dq, dk, dv = gpu_bwd(inp, o_st, lse32, w, bf16_arith=ab._lib.ATTN_BF16_FP16)
     ref = oracle.bwd_varlen(inp["q"], inp["k"], inp["v"], o_st, inp["dout"], lse32, inp["cu"], w.scale, w.causal,
                             w.window)
     for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
