@@ -119,7 +119,8 @@ def fwd_rows(q, k, v, scale, rows, causal=True, window=0):
 def make_o_lse(w, inputs, dtype=torch.float64):
     """O rounded to the workload's storage dtype and lse rounded to float32, from a forward pass
     over the drawn inputs.  Both sides of every comparison consume these same bytes."""
-    from attention_backward_amd.synth import DTYPES  # storage dtype table only
-
+    # storage dtype of a workload name (the oracle keeps its own table; it imports nothing of
+    # the HIP package)
+    DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16, "fp32": torch.float32}
     o, lse = fwd(inputs["q"], inputs["k"], inputs["v"], w.scale, w.causal, w.window, inputs["idx"], dtype=dtype)
     return o.to(DTYPES[w.dtype]), lse.to(torch.float32)
