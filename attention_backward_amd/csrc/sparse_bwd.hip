@@ -35,7 +35,9 @@ struct SpCfg {
   static constexpr int NV = DV / 32;     // 32-wide blocks of Dv
   static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims must be multiples of 32");
   static_assert(KQ % 2 == 0 && KV % 2 == 0, "k-steps split over two waves");
-  static_assert((HB * CQ) % 64 == 0 && (HB * CV) % 64 == 0, "rows split into wave loads");
+  static constexpr int LK = KC * CQ / 256;  // 16-byte gathers per thread: K rows of a chunk
+  static constexpr int LV = KC * CV / 256;  // V rows
+  static_assert((KC * CQ) % 256 == 0 && (KC * CV) % 256 == 0, "chunks split into whole workgroup loads");
 };
 
 // Tile rows are unpadded and their 16-byte chunk c sits at c ^ sw(row).  A Dqk = 576 row is
@@ -161,22 +163,32 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
   const int64_t kv0 = (int64_t)b * p.Skv * p.Hkv + g, nkv = (int64_t)p.B * p.Skv * p.Hkv;
   const i4v rk = buf_rsrc(p.k + kv0 * DQK, (uint64_t)(nkv - kv0) * DQK * 2);
   const i4v rv = buf_rsrc(p.v + kv0 * p.v_ld, (uint64_t)(nkv - kv0) * p.v_ld * 2);
+  // Tile slot s = 256 u + tid is physical chunk s % C of slot row s / C and holds logical chunk
+  // (s % C) ^ sw(row); each lane's slot row and column byte offset are computed once, so a
+  // gather costs one LDS read of the slot's key row and one multiply-add per load.
+  uint32_t krow[C::LK], kcol[C::LK], vrow[C::LV], vcol[C::LV];
+#pragma unroll
+  for (int u = 0; u < C::LK; u++) {
+    const int s = 256 * u + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sp_sw<DQK>(r);
+    krow[u] = (uint32_t)r;
+    kcol[u] = (uint32_t)(16 * ch);
+  }
+#pragma unroll
+  for (int u = 0; u < C::LV; u++) {
+    const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sp_sw<DV>(r);
+    vrow[u] = (uint32_t)r;
+    vcol[u] = (uint32_t)(16 * ch);
+  }
+  const uint32_t k_lds = lds_addr(&k_s[0][0]), v_lds = lds_addr(&v_s[0][0]);
+  const uint32_t kstride = (uint32_t)(p.Hkv * DQK * 2), vstride = (uint32_t)(p.Hkv * p.v_ld * 2);
   auto gather = [&](int c) {
     const int buf = c & 1, sb = c % 3;
+    const int *rows = row_s[sb];
+    const uint32_t kb = k_lds + buf * (C::KC * DQK * 2) + 1024 * w, vb = v_lds + buf * (C::KC * DV * 2) + 1024 * w;
 #pragma unroll
-    for (int u = 0; u < C::KC * C::CQ / 256; u++) {
-      const int s = 256 * u + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sp_sw<DQK>(r);
-      b2lds16(rk, ((uint32_t)row_s[sb][r] * p.Hkv * DQK + 8 * ch) * 2, &k_s[buf][(s - lane) * 8]);
-    }
-    if (C::KC * C::CQ % 256 != 0 && tid < C::KC * C::CQ % 256) {
-      const int s = C::KC * C::CQ / 256 * 256 + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sp_sw<DQK>(r);
-      b2lds16(rk, ((uint32_t)row_s[sb][r] * p.Hkv * DQK + 8 * ch) * 2, &k_s[buf][(s - lane) * 8]);
-    }
+    for (int u = 0; u < C::LK; u++) b2lds16_at(rk, (uint32_t)rows[krow[u]] * kstride + kcol[u], kb + 4096 * u);
 #pragma unroll
-    for (int u = 0; u < C::KC * C::CV / 256; u++) {
-      const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sp_sw<DV>(r);
-      b2lds16(rv, ((uint32_t)row_s[sb][r] * p.Hkv * p.v_ld + 8 * ch) * 2, &v_s[buf][(s - lane) * 8]);
-    }
+    for (int u = 0; u < C::LV; u++) b2lds16_at(rv, (uint32_t)rows[vrow[u]] * vstride + vcol[u], vb + 4096 * u);
   };
   // B[k][n] = tile[row = 16*ks + 8*hi + e][col = 32*nb + lo] by transposed reads of a row-major
   // [slot][d] tile: per 16-lane group, lanes 4r..4r+3 supply 16 columns of row r and lane i

@@ -57,8 +57,10 @@ struct SkCfg {
   static constexpr int KV = DV / 32;      // 16x16x32 k-steps over Dv
   static constexpr int NQ = DQK / 32;     // 32-wide blocks of dK
   static constexpr int NVW = DV / 128;    // 32-wide blocks of dV per wave (4 waves)
+  static constexpr int LQ = HB * CQ / 256;  // 16-byte loads per thread: Q tile
+  static constexpr int LD = HB * CV / 256;  // dO tile
   static_assert(DV % 128 == 0 && DQK % 32 == 0, "head dims");
-  static_assert((HB * CQ) % 64 == 0 && (HB * CV) % 64 == 0, "tile rows split into whole wave loads");
+  static_assert((HB * CQ) % 256 == 0 && (HB * CV) % 256 == 0, "tiles split into whole workgroup loads");
 };
 
 // dK blocks of wave v: [first, first + count) out of NQ (NQ = 18: 5, 5, 4, 4).
@@ -156,7 +158,21 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
 
   // Step t -> query i = i_beg + t / nhb, head block t % nhb.  Loads of a step: Q and dO rows of
   // its heads (rows past the group's end repeat its last head; masked below), lse and delta,
-  // and the count row of the 32 keys.
+  // and the count row of the 32 keys.  Tile slot s = 256 u + tid is physical chunk s % C of
+  // row s / C and holds logical chunk (s % C) ^ sw(row); the lanes' byte offsets for a full head
+  // block are computed once, and a ragged last block clamps its rows per step.
+  uint32_t qoff[C::LQ], doff[C::LD];
+#pragma unroll
+  for (int u = 0; u < C::LQ; u++) {
+    const int s = 256 * u + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sk_sw<DQK>(r);
+    qoff[u] = (uint32_t)(r * DQK + 8 * ch) * 2;
+  }
+#pragma unroll
+  for (int u = 0; u < C::LD; u++) {
+    const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sk_sw<DV>(r);
+    doff[u] = (uint32_t)(r * DV + 8 * ch) * 2;
+  }
+  const uint32_t q_lds = lds_addr(&q_s[0][0]), do_lds = lds_addr(&do_s[0][0]);
   auto issue = [&](int t, int buf) {
     const int i = i_beg + t / nhb, hb0 = (t % nhb) * C::HB;
     const int nh = min(C::HB, p.G - hb0);
@@ -164,19 +180,23 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
     const int64_t nrows = (int64_t)p.B * p.Sq * p.Hq;
     const i4v rq = buf_rsrc(p.q + qrow * DQK, (uint64_t)(nrows - qrow) * DQK * 2);
     const i4v rd = buf_rsrc(p.dout + qrow * DV, (uint64_t)(nrows - qrow) * DV * 2);
+    const uint32_t qb = q_lds + buf * (C::HB * DQK * 2) + 1024 * w, db = do_lds + buf * (C::HB * DV * 2) + 1024 * w;
+    if (nh == C::HB) {
 #pragma unroll
-    for (int u = 0; u < C::HB * C::CQ / 256; u++) {
-      const int s = 256 * u + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sk_sw<DQK>(r);
-      b2lds16(rq, (uint32_t)(min(r, nh - 1) * DQK + 8 * ch) * 2, &q_s[buf][(s - lane) * 8]);
-    }
-    if (C::HB * C::CQ % 256 != 0 && tid < C::HB * C::CQ % 256) {
-      const int s = C::HB * C::CQ / 256 * 256 + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sk_sw<DQK>(r);
-      b2lds16(rq, (uint32_t)(min(r, nh - 1) * DQK + 8 * ch) * 2, &q_s[buf][(s - lane) * 8]);
-    }
+      for (int u = 0; u < C::LQ; u++) b2lds16_at(rq, qoff[u], qb + 4096 * u);
 #pragma unroll
-    for (int u = 0; u < C::HB * C::CV / 256; u++) {
-      const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sk_sw<DV>(r);
-      b2lds16(rd, (uint32_t)(min(r, nh - 1) * DV + 8 * ch) * 2, &do_s[buf][(s - lane) * 8]);
+      for (int u = 0; u < C::LD; u++) b2lds16_at(rd, doff[u], db + 4096 * u);
+    } else {
+#pragma unroll
+      for (int u = 0; u < C::LQ; u++) {
+        const int s = 256 * u + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sk_sw<DQK>(r);
+        b2lds16_at(rq, (uint32_t)(min(r, nh - 1) * DQK + 8 * ch) * 2, qb + 4096 * u);
+      }
+#pragma unroll
+      for (int u = 0; u < C::LD; u++) {
+        const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sk_sw<DV>(r);
+        b2lds16_at(rd, (uint32_t)(min(r, nh - 1) * DV + 8 * ch) * 2, db + 4096 * u);
+      }
     }
     // One wave per small row (the LDS base of a direct load is per wave): lane l writes word l.
     if (w >= 2) {
