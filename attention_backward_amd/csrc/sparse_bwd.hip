@@ -315,6 +315,279 @@ __global__ __launch_bounds__(256, 1) void sparse_dq_kernel(const Params p) {
   }
 }
 
+// dQ kernel for head groups that are multiples of 64 in fp16 arithmetic (one product per operand;
+// the bf16 hi + lo form keeps the 32-head kernel above): one workgroup per (batch, query row, KV
+// head, block of 64 query heads).  The K and V rows of a chunk are gathered once for all 64
+// heads, half the gathers per product of the 32-head kernel.  Waves 0-1 form S for heads
+// 32*(w&1) .. +31 over the whole of Dqk from their resident Q rows; waves 2-3 form dP - delta over
+// the whole of Dv from their resident dO rows and hand it to the S waves through LDS; the S waves
+// form P and dS; then every wave adds dS K into its 32-wide d-blocks of dQ for all 64 heads (two
+// 32-row blocks sharing each B operand).
+template <class TT, int DQK, int DV>
+__global__ __launch_bounds__(256, 1) void sparse_dq64_kernel(const Params p) {
+  using C = SpCfg<DQK, DV>;
+  static_assert(!TT::SPLIT, "one product per operand");
+  constexpr int PF = 3, HB = 64;
+  __shared__ __attribute__((aligned(16))) short k_s[2][C::KC * DQK];
+  __shared__ __attribute__((aligned(16))) short v_s[2][C::KC * DV];
+  __shared__ __attribute__((aligned(16))) float dpm_s[2][16][64];  // dP - delta of waves 2-3, [register][lane]
+  __shared__ __attribute__((aligned(16))) short st_ds[HB * C::KC];  // dS [head][slot]
+  __shared__ int idx_s[3][C::KC];    // key of each slot, -1 where the slot is masked
+  __shared__ int row_s[3][C::KC];    // row gathered for each slot (a valid key of the chunk)
+  __shared__ int any_s[3];           // whether the chunk has a valid slot
+  __shared__ int idx_raw[4][C::KC];  // list entries of chunks c+1..c+3, loaded three chunks ahead
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5, lo = lane & 31;
+  const int i16 = lane & 15, g16 = lane >> 4;
+  const Factors fac = factors(p);
+  // Head blocks of one query row gather the same rows: placed 8 apart in the dispatch order, so
+  // that they run on one XCD at about the same time.
+  const int nhb = p.G / HB;
+  int x = blockIdx.x;
+  int hb;
+  {
+    const int grp = 8 * nhb, gi = x / grp, r = x % grp;
+    if ((gi + 1) * 8 <= p.B * p.Sq * p.Hkv) {
+      hb = r / 8;
+      x = gi * 8 + r % 8;
+    } else {
+      hb = r % nhb;
+      x = gi * 8 + r / nhb;
+    }
+  }
+  const int g = x % p.Hkv;
+  x /= p.Hkv;
+  const int i = x % p.Sq;
+  const int b = x / p.Sq;
+  const int h0 = g * p.G + hb * HB;  // first query head of this block
+  const int off = p.Skv - p.Sq;
+  const int64_t qrow = ((int64_t)b * p.Sq + i) * p.Hq;  // + h: BSHD row of (b, i, h)
+
+  // Resident A operands A[m = head][k = d] (32x32x16 layout) of the wave's 32 heads hw .. hw+31:
+  // Q rows (waves 0-1) or dO rows (waves 2-3) over the whole head dim.
+  const bool s_wave = w < 2;
+  const int hw = 32 * (w & 1);
+  constexpr int KA = C::KQ > C::KV ? C::KQ : C::KV;
+  const int nk = s_wave ? C::KQ : C::KV;
+  s8v ar[KA];
+  {
+    const int64_t r = qrow + h0 + hw + lo;
+#pragma unroll
+    for (int u = 0; u < KA; u++) {
+      const int kk = min(u, nk - 1);
+      ar[u] = s_wave ? *(const s8v *)(p.q + r * DQK + 16 * kk + 8 * hi) : *(const s8v *)(p.dout + r * DV + 16 * kk + 8 * hi);
+    }
+  }
+  // Per accumulator register r (row m = head hw + 8*(r/4) + 4*hi + r%4): lse for the S waves,
+  // minus delta for the dP waves (the dP accumulators start from it).
+  f16v lr;
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    const int64_t li = ((int64_t)b * p.Hq + h0 + hw + 8 * (r >> 2) + 4 * hi + (r & 3)) * p.Sq + i;
+    lr[r] = s_wave ? p.lse[li] : p.ndelta[li];
+  }
+
+  // dQ accumulators: d-blocks w, w+4, ... of both 32-head row blocks, for the whole walk.
+  constexpr int NQW = (C::NQ + 3) / 4;
+  f16v dq[2][NQW];
+#pragma unroll
+  for (int u = 0; u < NQW; u++) dq[0][u] = dq[1][u] = f16v{};
+
+  const int32_t *idx_row = p.idx + (((int64_t)b * p.Sq + i) * p.Hkv + g) * p.topk;
+  const int nchunks = (p.topk + C::KC - 1) / C::KC;
+  // Raw list entries of chunk c into idx_raw[c % 4] (wave 0, direct loads; entries past topk
+  // load the last entry and are dropped by the slot pass).
+  const i4v ridx = buf_rsrc(idx_row, (uint64_t)p.topk * 4);
+  auto load_idx = [&](int c) {
+    if (w == 0 && lane < C::KC) b2lds4(ridx, (uint32_t)min(c * C::KC + lane, p.topk - 1) * 4, &idx_raw[c & 3][0]);
+  };
+  // Slots of chunk c (one wave): a masked slot (padding, out of range, past the causal diagonal)
+  // gathers the row of the chunk's first valid slot; its own dS is forced to zero.
+  auto slots = [&](int c) {
+    const int sb = c % 3;
+    int j = -1;
+    if (lane < C::KC) {
+      const int t = c * C::KC + lane;
+      j = t < p.topk ? idx_raw[c & 3][lane] : -1;
+      if (j < 0 || j >= p.Skv || (p.causal && j > i + off)) j = -1;
+    }
+    const uint64_t m = __ballot(j >= 0);
+    const int first = m ? __shfl(j, __builtin_ctzll(m)) : 0;
+    if (lane < C::KC) {
+      idx_s[sb][lane] = j;
+      row_s[sb][lane] = j >= 0 ? j : first;
+    }
+    if (lane == 0) any_s[sb] = m != 0;
+  };
+  // Gathers through buffer resources over this (batch, KV head)'s K and V rows (the host checks
+  // that every byte offset fits 32 bits); lane slot rows and column offsets computed once.
+  const int64_t kv0 = (int64_t)b * p.Skv * p.Hkv + g, nkv = (int64_t)p.B * p.Skv * p.Hkv;
+  const i4v rk = buf_rsrc(p.k + kv0 * DQK, (uint64_t)(nkv - kv0) * DQK * 2);
+  const i4v rv = buf_rsrc(p.v + kv0 * p.v_ld, (uint64_t)(nkv - kv0) * p.v_ld * 2);
+  // Per load: slot row in the high half, column byte offset in the low half (one register each).
+  uint32_t kslot[C::LK], vslot[C::LV];
+#pragma unroll
+  for (int u = 0; u < C::LK; u++) {
+    const int s = 256 * u + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sp_sw<DQK>(r);
+    kslot[u] = (uint32_t)r << 16 | (uint32_t)(16 * ch);
+  }
+#pragma unroll
+  for (int u = 0; u < C::LV; u++) {
+    const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sp_sw<DV>(r);
+    vslot[u] = (uint32_t)r << 16 | (uint32_t)(16 * ch);
+  }
+  const uint32_t k_lds = lds_addr(&k_s[0][0]), v_lds = lds_addr(&v_s[0][0]);
+  const uint32_t kstride = (uint32_t)(p.Hkv * DQK * 2), vstride = (uint32_t)(p.Hkv * p.v_ld * 2);
+  auto gather = [&](int c) {
+    const int buf = c & 1;
+    const int *rows = row_s[c % 3];
+    const uint32_t kb = k_lds + buf * (C::KC * DQK * 2) + 1024 * w, vb = v_lds + buf * (C::KC * DV * 2) + 1024 * w;
+#pragma unroll
+    for (int u = 0; u < C::LK; u++)
+      b2lds16_at(rk, (uint32_t)rows[kslot[u] >> 16] * kstride + (kslot[u] & 0xffffu), kb + 4096 * u);
+#pragma unroll
+    for (int u = 0; u < C::LV; u++)
+      b2lds16_at(rv, (uint32_t)rows[vslot[u] >> 16] * vstride + (vslot[u] & 0xffffu), vb + 4096 * u);
+  };
+  // LDS read offsets of a lane within a tile, as (per-lane base + compile-time constant) so that
+  // the constants fold into the reads' offset fields:
+  //  natural read of slot row lo, logical chunk x = 2*kk + hi: the swizzle (below 16) only
+  //   changes the low 4 bits of x, so chunk = 16*(kk/8) + ((2*(kk%8) + hi) ^ sw) and the byte
+  //   offset is nat[kk % 8] + 256*(kk / 8);
+  //  transposed read (B[k = slot 16*ks + 8*hi + e][n = d 32*nb + lo]) of row 16*ks + 8*hi +
+  //   4*half + i16/4, column 32*nb + 16*(g16&1) + 4*(i16&3): the row's swizzle does not depend
+  //   on ks and changes only the low 3 bits of the chunk 4*nb + t, so the byte offset is
+  //   tr[half][nb % 2] + 18432*ks + 128*(nb / 2) (Dqk = 576).
+  static_assert(DQK == 576, "transposed-read offsets assume 1152-byte rows");
+  uint32_t nat[8], tr[2][2];
+  {
+    const int rowlen = s_wave ? DQK : DV;
+    const int sw = s_wave ? sp_sw<DQK>(lo) : sp_sw<DV>(lo);
+#pragma unroll
+    for (int j = 0; j < 8; j++) nat[j] = (uint32_t)(2 * lo * rowlen + 16 * ((2 * j + hi) ^ sw));
+    const int r4 = i16 >> 2, t = 2 * (g16 & 1) + ((i16 & 3) >> 1);
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+      const int row = 8 * hi + 4 * half + r4, swr = sp_sw<DQK>(row);
+#pragma unroll
+      for (int par = 0; par < 2; par++)
+        tr[half][par] = (uint32_t)(2 * DQK * row + 16 * ((4 * par + t) ^ swr) + 8 * (i16 & 1));
+    }
+  }
+
+#pragma unroll
+  for (int c = 0; c < 3; c++)
+    if (c < nchunks) load_idx(c);
+  wait_vm0();
+  __syncthreads();
+  if (w == 0) slots(0);
+  __syncthreads();
+  gather(0);
+  if (w == 0 && nchunks > 1) slots(1);
+  wait_vm0();
+  __syncthreads();
+
+  for (int c = 0; c < nchunks; c++) {
+    const int buf = c & 1, sb = c % 3;
+    if (c + 1 < nchunks) gather(c + 1);    // rows of chunk c+1 became visible at the last barrier
+    if (c + 3 < nchunks) load_idx(c + 3);  // consumed by slots(c + 3) in the next iteration
+
+    // Phase A: S = Q K^T (waves 0-1) or dP - delta = dO V^T - delta (waves 2-3) for the wave's
+    // 32 heads over the whole head dim; M = heads, N = slots; B = K / V rows of the slots,
+    // natural reads through a ring; two accumulators so that consecutive products are
+    // independent.
+    f16v acc;
+    {
+      const uint32_t tile = s_wave ? lds_addr(k_s[buf]) : lds_addr(v_s[buf]);
+      uint32_t ab[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) ab[j] = lds_base_add(tile, nat[j]);
+      f16v a0 = s_wave ? f16v{} : lr, a1 = f16v{};
+      ring_pipeline<KA, PF>(
+          [&](int u) {
+            const int kk = min(u, nk - 1);
+            return lds_rd16_at(ab[kk % 8] + 256 * (kk / 8));
+          },
+          [&](int u, s8v bv) {
+            if (u < nk) {
+              if (u & 1)
+                a1 = TT::mfma(ar[u], bv, a1);
+              else
+                a0 = TT::mfma(ar[u], bv, a0);
+            }
+          });
+      acc = a0 + a1;
+    }
+    if (!s_wave) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) dpm_s[w - 2][r][lane] = acc[r];
+    }
+    __syncthreads();  // dP - delta visible
+    // Phase B (S waves): P = exp2(S c - lse) and dS = P (dP - delta) of register r: head
+    // hw + 8*(r/4) + 4*hi + r%4, slot lo; masked slots give 0.  A dP wave finds the slots of
+    // chunk c+2 meanwhile.
+    if (s_wave) {
+      const bool slot_ok = idx_s[sb][lo] >= 0;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float pr = exp2f_hw(acc[r] * fac.c - lr[r]);
+        const float ds = slot_ok ? ds_of<TT>(pr, dpm_s[w][r][lane], fac) : 0.f;
+        st_ds[(hw + 8 * (r >> 2) + 4 * hi + (r & 3)) * C::KC + lo] = TT::cvt(ds);
+      }
+    } else if (w == 2 && c + 2 < nchunks) {
+      slots(c + 2);  // read after the next barrier
+    }
+    __syncthreads();  // dS visible
+    // Phase C: dQ += dS K for this wave's d-blocks and both row blocks; A = dS[m = head 32*mb + lo]
+    // [k = slots 16*ks + 8*hi + e] (natural reads), B = K^T by transposed reads through a ring,
+    // shared by the two row blocks.  A chunk with no valid slot contributes nothing.
+    if (any_s[sb]) {
+      s8v da[2][2];
+#pragma unroll
+      for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) da[mb][ks] = *(const s8v *)&st_ds[(32 * mb + lo) * C::KC + 16 * ks + 8 * hi];
+      uint32_t at[2][2];
+#pragma unroll
+      for (int half = 0; half < 2; half++)
+#pragma unroll
+        for (int par = 0; par < 2; par++) at[half][par] = lds_base_add(lds_addr(k_s[buf]), tr[half][par]);
+      ring_pipeline<2 * NQW, PF>(
+          [&](int n) {
+            const int ks = n / NQW, nb = min(w + 4 * (n % NQW), C::NQ - 1);
+            return cat8(lds_tr4_at(at[0][nb % 2] + 18432 * ks + 128 * (nb / 2)),
+                        lds_tr4_at(at[1][nb % 2] + 18432 * ks + 128 * (nb / 2)));
+          },
+          [&](int n, s8v bb) {
+            const int ks = n / NQW, u = n % NQW;
+            if (w + 4 * u < C::NQ) {
+              dq[0][u] = TT::mfma(da[0][ks], bb, dq[0][u]);
+              dq[1][u] = TT::mfma(da[1][ks], bb, dq[1][u]);
+            }
+          });
+    }
+    wait_vm0();
+    __syncthreads();  // chunk c+1 landed, its successor's slots visible; chunk c consumed
+  }
+
+  // dQ = scale * acc (row m = head 32*mb + 8*(r/4) + 4*hi + r%4, column 32*nb + lo).
+#pragma unroll
+  for (int u = 0; u < NQW; u++) {
+    const int nb = w + 4 * u;
+    if (nb < C::NQ) {
+#pragma unroll
+      for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int m = 32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          p.dq[(qrow + h0 + m) * DQK + 32 * nb + lo] = TT::cvt_out(dq[mb][u][r] * fac.dq);
+        }
+    }
+  }
+}
+
 // Landing pass: dk = scale * dk_acc, dv = dv_acc, cast to the storage dtype (8 elements per
 // thread, 32-byte reads and 16-byte writes).
 template <class TT>
@@ -376,8 +649,21 @@ hipError_t launch_zero(float *buf, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
+#ifndef ATTN_SPARSE_DQ64
+#define ATTN_SPARSE_DQ64 1
+#endif
+
 hipError_t launch_sparse_dq(const Params &p, int arith, hipStream_t st) {
   if (p.Dqk != 576 || p.Dv != 512) return hipErrorInvalidValue;
+  if (ATTN_SPARSE_DQ64 && arith != ARITH_BF16 && p.G % 64 == 0) {
+    const int64_t blocks = (int64_t)p.B * p.Sq * p.Hkv * (p.G / 64);
+    if (blocks < 1) return hipSuccess;
+    if (arith == ARITH_F16B)
+      hipLaunchKernelGGL((sparse_dq64_kernel<F16B, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((sparse_dq64_kernel<F16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
   const int nhb = (p.G + SpCfg<576, 512>::HB - 1) / SpCfg<576, 512>::HB;
   const int64_t blocks = (int64_t)p.B * p.Sq * p.Hkv * nhb;
   if (blocks < 1) return hipSuccess;

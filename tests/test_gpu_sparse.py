@@ -37,6 +37,10 @@ SMALL = [
     sparse("g40_noncausal", Sq=33, Skv=90, Hq=40, Hkv=1, causal=False, topk=64, seed=202),
     # Sq > Skv: the first queries see no key at all (empty rows)
     sparse("causal_sq_gt_skv", Sq=80, Skv=50, Hq=32, Hkv=1, topk=20, seed=203),
+    # fp16 with G = 64 (one workgroup per query row and KV head covers every head), two KV heads
+    sparse("mla_h64_fp16_two_kv", B=2, Sq=37, Skv=80, Hq=128, Hkv=2, dtype="fp16", topk=40, seed=204),
+    # fp16 with G = 128: two 64-head blocks of one query row
+    sparse("g128_fp16", Sq=20, Skv=45, Hq=128, Hkv=1, dtype="fp16", topk=33, seed=205),
 ]
 
 
@@ -65,9 +69,10 @@ def test_sparse_small_full_parity(w):
             assert torch.all(dv[b, ~torch.from_numpy(sel), g] == 0)
 
 
-def test_sparse_duplicates_and_out_of_range_entries():
+@pytest.mark.parametrize("hq,dtype", [(32, "bf16"), (64, "fp16")])
+def test_sparse_duplicates_and_out_of_range_entries(hq, dtype):
     """Each occurrence of a key counts; negative, too-large and (causal) future entries are dropped."""
-    w = sparse("dups", Sq=48, Skv=96, Hq=32, Hkv=1, topk=72, seed=210)
+    w = sparse("dups", Sq=48, Skv=96, Hq=hq, Hkv=1, dtype=dtype, topk=72, seed=210)
     inp = synth.make_inputs(w)
     rng = np.random.default_rng(211)
     idx = inp["idx"].numpy().copy()
