@@ -172,8 +172,48 @@ def test_masked_keys_do_not_matter():
     assert torch.all(a[1][:, :697] == 0) and torch.all(a[2][:, :697] == 0)
 
 
-FULL = ["mha_causal_b2_s2048_h32_d128_fp16", "gqa_causal_b1_t16384_hq32_hkv4_d128_bf16",
-        "swa_gqa_b2_t8192_hq16_hkv8_d64_w1024_fp16", "swa_gqa_b2_t8000_hq16_hkv8_d64_w1024_fp16"]
+# Sampled rows (edges, tile boundaries, random rows) of the workloads not compared in full below.
+FULL = ["gqa_causal_b1_t16384_hq32_hkv4_d128_bf16"]
+
+
+# Every element of the output against the full oracle backward, in the benchmark's launch
+# configuration.
+EVERY = ["mha_causal_b2_s2048_h32_d128_fp16", "swa_gqa_b2_t8192_hq16_hkv8_d64_w1024_fp16",
+         "swa_gqa_b2_t8000_hq16_hkv8_d64_w1024_fp16"]
+
+
+@pytest.mark.parametrize("name", EVERY)
+def test_full_size_every_element(name):
+    log(f"case {name} (full size, every element)")
+    full_compare(W[name])
+
+
+def group_slice(inp, w, g):
+    """The sub-problem of KV head g: its G query heads and its K/V rows.  Heads of different groups
+    never interact, so the oracle's full backward over this slice gives every dq row of those
+    heads and every dk/dv row of KV head g."""
+    G = w.Hq // w.Hkv
+    hs = slice(g * G, (g + 1) * G)
+    q, o, do = (inp[n][:, :, hs].contiguous() for n in ("q", "o", "dout"))
+    k, v = (inp[n][:, :, g : g + 1].contiguous() for n in ("k", "v"))
+    lse = inp["lse"][:, hs].contiguous()
+    idx = None if inp["idx"] is None else inp["idx"][:, :, g : g + 1].contiguous()
+    return oracle.bwd(q, k, v, o, do, lse, w.scale, w.causal, w.window, idx), hs
+
+
+def test_full_size_gqa_one_group_every_row():
+    """The 16K-token GQA workload: every dq row of one KV group's 8 query heads and every dk/dv
+    row of that KV head (the last group, batch 0)."""
+    name = "gqa_causal_b1_t16384_hq32_hkv4_d128_bf16"
+    w = W[name]
+    log(f"case {name} (full size, every row of KV group {w.Hkv - 1})")
+    inp = prepare(w)
+    dq, dk, dv = run(inp, w)
+    g = w.Hkv - 1
+    (rq, rk, rv), hs = group_slice(inp, w, g)
+    check_close("dq group", dq[:, :, hs].double().numpy(), rq)
+    check_close("dk group", dk[:, :, g : g + 1].double().numpy(), rk)
+    check_close("dv group", dv[:, :, g : g + 1].double().numpy(), rv)
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -112,6 +112,18 @@ def test_sparse_full_size_sampled_parity():
     check_close("dv rows", dv[krows[:, 0], krows[:, 1], krows[:, 2]].double().numpy(), ref_dv)
     for t in (dq, dk, dv):
         assert torch.isfinite(t.float()).all()
+    # every dq row of one (batch, head) slice: query head 37, all 4096 query rows
+    h = 37
+    allq = np.array([(0, i, h) for i in range(w.Sq)], np.int64)
+    check_close(f"dq head {h}, every row", dq[0, :, h].double().numpy(),
+                oracle.bwd_dq_rows(*args, allq, w.causal, w.window, inp["idx"]))
+    # contiguous key blocks of the KV head: the first keys (every query may list them), a block in
+    # the middle, and the last keys (listed by the last queries only)
+    kb = np.array([(0, j, 0) for j in list(range(0, 64)) + list(range(4064, 4128)) + list(range(w.Skv - 64, w.Skv))],
+                  np.int64)
+    bk, bv = oracle.bwd_dkv_rows(*args, kb, w.causal, w.window, inp["idx"])
+    check_close("dk key blocks", dk[0, kb[:, 1], 0].double().numpy(), bk)
+    check_close("dv key blocks", dv[0, kb[:, 1], 0].double().numpy(), bv)
     # unattended keys: exactly zero
     idx = inp["idx"].numpy().reshape(-1)
     sel = np.zeros(w.Skv, bool)

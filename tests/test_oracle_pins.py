@@ -176,6 +176,38 @@ def test_bruteforce_dense(c):
     np.testing.assert_allclose(oracle.delta(o16, do), np.einsum("bihd,bihd->bhi", o16, do), rtol=1e-13, atol=1e-13)
 
 
+@pytest.mark.parametrize(
+    "name,window",
+    [("mha_causal_b1_s256_h2_d128_fp16", 0), ("mha_causal_b1_s256_h2_d128_fp16", 40)],
+)
+def test_bruteforce_at_workload_size(name, window):
+    """The oracle against the dense numpy restatement at the size of the smallest workload (and a
+    sliding window on the same inputs), on the workload's own seeded inputs in f64."""
+    from attention_backward_amd import synth
+
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    q, k, v, do = (inp[n].double().numpy() for n in ("q", "k", "v", "dout"))
+    o, lse = bf.forward(q, k, v, w.scale, w.causal, window)
+    got = oracle.bwd(q, k, v, o, do, lse, w.scale, w.causal, window)
+    want = bf.backward(q, k, v, o, do, lse, w.scale, w.causal, window)
+    for g, x in zip(got, want):
+        np.testing.assert_allclose(g, x, rtol=1e-10, atol=1e-12)
+
+
+def test_bruteforce_top_k_latent_shape():
+    """A small top-k case with the latent head dims (Dqk = 576, Dv = 512) and 16 query heads on one
+    KV head, lists with padding, out-of-range and duplicate entries."""
+    q, k, v, do = rnd(31, 1, 24, 40, 16, 1, 576, 512)
+    idx = rnd_idx(32, 1, 24, 40, 1, 12)
+    scale = 1.0 / math.sqrt(576)
+    o, lse = bf.forward(q, k, v, scale, True, 0, idx)
+    got = oracle.bwd(q, k, v, o, do, lse, scale, True, 0, idx)
+    want = bf.backward(q, k, v, o, do, lse, scale, True, 0, idx)
+    for g, x in zip(got, want):
+        np.testing.assert_allclose(g, x, rtol=1e-10, atol=1e-12)
+
+
 @pytest.mark.parametrize("c", CASES)
 def test_invariants(c):
     q, k, v, do, idx, scale, causal, window = case_inputs(c, seed=9)
