@@ -27,8 +27,11 @@ struct F16CopySet {
 };
 
 // maxbits[group] = max over the group's tensors of the bf16 bits with the sign cleared, which
-// order like the magnitudes (inf and NaN above every finite value).  One atomic per wave.
+// order like the magnitudes (inf and NaN above every finite value).  The workgroup reduces in
+// registers and LDS first and issues one atomic: atomics on one address retire one at a time, and
+// one per wave (tens of thousands over a large tensor) made this pass slower than the copy.
 __global__ __launch_bounds__(256) void absmax_kernel(const F16CopySet cs, unsigned *__restrict__ maxbits) {
+  __shared__ unsigned wmax[4];
   const F16Copy c = cs.c[blockIdx.y];
   const int64_t n8 = c.n / 8;
   unsigned m = 0;
@@ -39,7 +42,12 @@ __global__ __launch_bounds__(256) void absmax_kernel(const F16CopySet cs, unsign
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, o));
-  if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(&maxbits[c.group], m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    if (m != 0) atomicMax(&maxbits[c.group], m);
+  }
 }
 
 // One power of two per group: 2^e with e = 15 - E where max = f 2^E, f in [0.5, 1), so the largest
