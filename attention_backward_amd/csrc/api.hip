@@ -278,7 +278,9 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
     float *dv_acc = (float *)((char *)dk_acc + dk_acc_bytes(a));
     uint16_t *cnt = (uint16_t *)((char *)dv_acc + dv_acc_bytes(a));
     const int64_t nk = a->B * a->Skv * a->Hkv * a->Dqk, nv = a->B * a->Skv * a->Hkv * a->Dv;
-    const size_t zero_bytes = dk_acc_bytes(a) + dv_acc_bytes(a) + cnt_bytes(a);  // contiguous
+    // contiguous; the count rows need no zero-fill when each is written whole
+    const size_t zero_bytes =
+        dk_acc_bytes(a) + dv_acc_bytes(a) + (attn::topk_count_by_rows((int)skv_pad(a)) ? 0 : cnt_bytes(a));
     if (e == hipSuccess) e = attn::launch_zero(dk_acc, (int64_t)(zero_bytes / 4), st);
     if (e == hipSuccess)
       e = attn::launch_topk_count(a->topk_idx, cnt, a->B, a->Sq, a->Skv, a->Hkv, a->topk, (int)skv_pad(a), a->causal,

@@ -49,6 +49,10 @@ hipError_t launch_dense_fwd(const FwdParams &p, int D, bool bf16, hipStream_t st
 //   launch_land_kv     out [rows, Dqk] = storage(scale * dk_acc + [dv_acc, 0]) (shared-latent dKV;
 //                      with rescale: rescale[2] * dk_acc + rescale[3] * [dv_acc, 0]).
 hipError_t launch_zero(float *buf, int64_t n, hipStream_t st);
+// Rows of up to kCountRowLdsMax bytes are counted one list per workgroup in LDS and written whole
+// (no zero-fill needed); longer rows use global atomics on a zero-filled mask.
+constexpr int kCountRowLdsMax = 65536;
+bool topk_count_by_rows(int skv_pad);
 hipError_t launch_topk_count(const int32_t *idx, uint16_t *cnt, int64_t B, int64_t Sq, int64_t Skv, int64_t Hkv,
                              int64_t topk, int skv_pad, int causal, hipStream_t st);
 hipError_t launch_sparse_dq(const Params &p, int arith, hipStream_t st);

@@ -47,6 +47,30 @@ __global__ __launch_bounds__(256) void topk_count_kernel(const int32_t *__restri
   }
 }
 
+// The same counts, one list per workgroup: the row [skv_pad] is built in LDS (LDS atomics) and
+// written out whole, zeros included, so it needs no zero-fill beforehand and no global atomics.
+// Row (b, i, g) of the lists is row ((b * Hkv + g) * Sq + i) of cnt.
+__global__ __launch_bounds__(256) void topk_count_rows_kernel(const int32_t *__restrict__ idx, uint32_t *__restrict__ cnt,
+                                                              int topk, int Sq, int Skv, int Hkv, int skv_pad, int causal) {
+  extern __shared__ uint32_t crow[];  // skv_pad / 2 words, two 16-bit counts each
+  const int64_t row = blockIdx.x;     // (b, i, g) in [B, Sq, Hkv] order
+  const int g = (int)(row % Hkv);
+  const int i = (int)((row / Hkv) % Sq);
+  const int64_t b = row / ((int64_t)Hkv * Sq);
+  const int nw = skv_pad / 2;
+  for (int t = threadIdx.x; t < nw; t += 256) crow[t] = 0;
+  __syncthreads();
+  const int off = Skv - Sq;
+  for (int x = threadIdx.x; x < topk; x += 256) {
+    const int j = idx[row * topk + x];
+    if (j < 0 || j >= Skv || (causal && j > i + off)) continue;
+    atomicAdd(&crow[j >> 1], 1u << (16 * (j & 1)));
+  }
+  __syncthreads();
+  uint32_t *dst = cnt + ((b * Hkv + g) * Sq + i) * (int64_t)nw;
+  for (int t = threadIdx.x; t < nw; t += 256) dst[t] = crow[t];
+}
+
 template <int DQK, int DV>
 struct SkCfg {
   static constexpr int BM = 32;           // keys per workgroup
@@ -347,8 +371,17 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
   }
 }
 
+bool topk_count_by_rows(int skv_pad) { return (int64_t)skv_pad * 2 <= kCountRowLdsMax; }
+
 hipError_t launch_topk_count(const int32_t *idx, uint16_t *cnt, int64_t B, int64_t Sq, int64_t Skv, int64_t Hkv,
                              int64_t topk, int skv_pad, int causal, hipStream_t st) {
+  if (topk_count_by_rows(skv_pad)) {
+    const int64_t rows = B * Sq * Hkv;
+    if (rows < 1) return hipSuccess;
+    hipLaunchKernelGGL(topk_count_rows_kernel, dim3((unsigned)rows), dim3(256), (size_t)skv_pad * 2, st, idx,
+                       (uint32_t *)cnt, (int)topk, (int)Sq, (int)Skv, (int)Hkv, skv_pad, causal);
+    return hipGetLastError();
+  }
   const int64_t n = B * Sq * Hkv * topk;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 16384) blocks = 16384;
