@@ -104,10 +104,11 @@ size_t queue_bytes(const attn_bwd_args *a) {
   if (!dkdv_queue(a)) return 0;
   return 256 + (dkdv_hsplit(a) > 1 ? 2 * part_bytes(a) : 0);
 }
-// bf16 calls re-expressed in fp16 (f16_prepass.hip): a 256-byte block (largest magnitudes, scales
-// and the factors that undo them) and scaled fp16 copies of q, k, v (none in the shared-latent
-// form, where V is part of K's rows), o and dout.  Automatic choice: from 2^22 elements of q up
+// bf16 calls re-expressed in fp16 (f16_prepass.hip): a 1280-byte block (largest magnitudes in
+// 4 x 64 slots, scales and the factors that undo them) and scaled fp16 copies of q, k, v (none in
+// the shared-latent form, where V is part of K's rows), o and dout.  Automatic choice: from 2^22 elements of q up
 // (the copies cost about three passes over the inputs; the hi + lo products cost more there).
+constexpr size_t kF16xHeader = 1280;  // maxbits [4][64] u32, then scales[4] and rescale[5] f32
 bool f16x(const attn_bwd_args *a) {
   if (a->dtype != ATTN_DT_BF16) return false;
   if (a->bf16_arith == ATTN_BF16_FP16) return true;
@@ -116,7 +117,7 @@ bool f16x(const attn_bwd_args *a) {
 size_t f16x_bytes(const attn_bwd_args *a) {
   if (!f16x(a)) return 0;
   const size_t nq = (size_t)(a->B * a->Sq * a->Hq), nk = (size_t)(a->B * a->Skv * a->Hkv);
-  size_t n = 256 + align256(nq * a->Dqk * 2) + align256(nk * a->Dqk * 2) + 2 * align256(nq * a->Dv * 2);
+  size_t n = kF16xHeader + align256(nq * a->Dqk * 2) + align256(nk * a->Dqk * 2) + 2 * align256(nq * a->Dv * 2);
   if (!a->kv_shared) n += align256(nk * a->Dv * 2);
   return n;
 }
@@ -223,9 +224,9 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
   if (arith == attn::ARITH_F16B) {
     // Scaled fp16 copies of the inputs; the kernels then read them and the factors in `rescale`.
     unsigned *maxbits = (unsigned *)fx;
-    float *scales = (float *)(fx + 16), *rescale = (float *)(fx + 32);
+    float *scales = (float *)(fx + 4 * 4 * attn::kMaxSlots), *rescale = scales + 4;
     const size_t nq = (size_t)(a->B * a->Sq * a->Hq), nk = (size_t)(a->B * a->Skv * a->Hkv);
-    char *cur = fx + 256;
+    char *cur = fx + kF16xHeader;
     auto take = [&](size_t elems) {
       short *r = (short *)cur;
       cur += align256(elems * 2);
@@ -241,7 +242,7 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
     if (!shared) cp[ncp++] = attn::F16Copy{p.v, v16, (int64_t)(nk * a->Dv), 2};
     cp[ncp++] = attn::F16Copy{p.o, o16, (int64_t)(nq * a->Dv), shared ? 1 : 2};  // O carries V's scale
     cp[ncp++] = attn::F16Copy{p.dout, do16, (int64_t)(nq * a->Dv), 3};
-    if (e == hipSuccess) e = attn::launch_zero((float *)fx, 64, st);
+    if (e == hipSuccess) e = attn::launch_zero((float *)fx, 4 * attn::kMaxSlots, st);  // the slots
     if (e == hipSuccess) e = attn::launch_f16_prepass(cp, ncp, maxbits, scales, rescale, p.c, p.scale, st);
     p.q = q16;
     p.k = k16;

@@ -22,14 +22,16 @@
 namespace attn {
 
 constexpr int kMaxCopies = 5;
+static_assert(kMaxSlots > 0, "largest-magnitude slots per group");
 struct F16CopySet {
   F16Copy c[kMaxCopies];
 };
 
-// maxbits[group] = max over the group's tensors of the bf16 bits with the sign cleared, which
-// order like the magnitudes (inf and NaN above every finite value).  The workgroup reduces in
-// registers and LDS first and issues one atomic: atomics on one address retire one at a time, and
-// one per wave (tens of thousands over a large tensor) made this pass slower than the copy.
+// maxbits[group][slot] = max over the group's tensors of the bf16 bits with the sign cleared, which
+// order like the magnitudes (inf and NaN above every finite value).  Atomics on one address retire
+// one at a time (about 10 ns each, measured), so the workgroup reduces in registers and LDS first
+// and its one atomic goes to slot blockIdx.x % kMaxSlots of its group; the finalize pass reduces
+// the slots.
 __global__ __launch_bounds__(256) void absmax_kernel(const F16CopySet cs, unsigned *__restrict__ maxbits) {
   __shared__ unsigned wmax[4];
   const F16Copy c = cs.c[blockIdx.y];
@@ -46,7 +48,7 @@ __global__ __launch_bounds__(256) void absmax_kernel(const F16CopySet cs, unsign
   __syncthreads();
   if (threadIdx.x == 0) {
     m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-    if (m != 0) atomicMax(&maxbits[c.group], m);
+    if (m != 0) atomicMax(&maxbits[c.group * kMaxSlots + blockIdx.x % kMaxSlots], m);
   }
 }
 
@@ -59,7 +61,9 @@ __global__ void f16_finalize_kernel(const unsigned *__restrict__ maxbits, float 
   float s[4];
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    const float m = __uint_as_float(maxbits[t] << 16);
+    unsigned mb = 0;
+    for (int k = 0; k < kMaxSlots; k++) mb = max(mb, maxbits[t * kMaxSlots + k]);
+    const float m = __uint_as_float(mb << 16);
     int e = 0;
     if (m > 0.f && m <= 3.3895314e38f) {
       int E;

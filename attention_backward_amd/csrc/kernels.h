@@ -64,9 +64,10 @@ hipError_t launch_land_kv(const float *dk_acc, const float *dv_acc, short *out, 
                           float scale, const float *rescale, bool bf16, hipStream_t st);
 
 // Re-expression of bf16 inputs in fp16.  Tensors: 0 q, 1 k, 2 v (with o, which shares v's
-// scale), 3 dout.  launch_f16_prepass: maxbits[4] (zeroed by the caller) = the largest bf16
-// magnitude of each group; then one power-of-two scale per group, the factors rescale[4] that
-// undo them (exponent scale, dQ, dK, dV) and the scaled fp16 copies.
+// scale), 3 dout.  launch_f16_prepass: maxbits[4][kMaxSlots] (zeroed by the caller) = the largest
+// bf16 magnitudes of each group, spread over slots; then one power-of-two scale per group, the
+// factors rescale[5] that undo them (exponent scale, dQ, dK, dV, dS) and the scaled fp16 copies.
+constexpr int kMaxSlots = 64;
 struct F16Copy {
   const short *src;  // bf16
   short *dst;        // fp16 copy

@@ -185,11 +185,12 @@ def test_forward_varlen_entry_point_validates(kw, status):
 
 
 def test_bf16_reexpression_workspace():
-    """bf16 calls computed on fp16 copies add a 256-byte block and the copies of q, k, v, o, dout;
-    the automatic choice takes that path from 2^22 elements of q on, fp16 calls never."""
+    """bf16 calls computed on fp16 copies add a 1280-byte block (largest magnitudes in 4 x 64
+    slots, scales, factors) and the copies of q, k, v, o, dout; the automatic choice takes that
+    path from 2^22 elements of q on, fp16 calls never."""
     rows = 2 * (2 * 32 * 2048 * 4)
     nq, nk = 2 * 2048 * 32 * 128, 2 * 2048 * 8 * 128
-    copies = 256 + 2 * nq + 2 * nk + 2 * nk + 2 * (2 * nq)
+    copies = 1280 + 2 * nq + 2 * nk + 2 * nk + 2 * (2 * nq)
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=8, dtype=1, bf16_arith=2)) == rows + copies
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=8, dtype=1, bf16_arith=0)) == rows + copies  # 2^24 elements
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=8, dtype=1, bf16_arith=1)) == rows
