@@ -106,13 +106,27 @@ size_t queue_bytes(const attn_bwd_args *a) {
 }
 // bf16 calls re-expressed in fp16 (f16_prepass.hip): a 1280-byte block (largest magnitudes in
 // 4 x 64 slots, scales and the factors that undo them) and scaled fp16 copies of q, k, v (none in
-// the shared-latent form, where V is part of K's rows), o and dout.  Automatic choice: from 2^22 elements of q up
-// (the copies cost about three passes over the inputs; the hi + lo products cost more there).
+// the shared-latent form, where V is part of K's rows), o and dout.
 constexpr size_t kF16xHeader = 1280;  // maxbits [4][64] u32, then scales[4] and rescale[5] f32
+// Automatic choice between the two bf16 forms, from a cost estimate.  The hi + lo form adds the
+// second P and dS products, 4 Dqk flops per (query, key, head) pair; they measured about
+// 1.2 PFLOP/s.  The re-expression costs three passes over q, k, v, o and dout, which measured about
+// 6.5 TB/s, plus a few launches.  Keys per query: the list length, the window, half the keys
+// under a causal mask, or all of them (packed calls: of the longest sequence).
 bool f16x(const attn_bwd_args *a) {
   if (a->dtype != ATTN_DT_BF16) return false;
   if (a->bf16_arith == ATTN_BF16_FP16) return true;
-  return a->bf16_arith == ATTN_BF16_AUTO && a->B * a->Sq * a->Hq * a->Dqk >= ((int64_t)1 << 22);
+  if (a->bf16_arith != ATTN_BF16_AUTO) return false;
+  const double skv = (double)(a->cu_seqlens ? a->max_seqlen : a->Skv);
+  const double kpq = a->topk_idx ? (double)a->topk
+                     : a->window > 0 ? (a->window < skv ? (double)a->window : skv)
+                     : a->causal ? skv / 2 : skv;
+  const double pairs = (double)a->B * a->Sq * a->Hq * kpq;
+  const double nq = (double)a->B * a->Sq * a->Hq, nk = (double)a->B * a->Skv * a->Hkv;
+  const double bytes = 2.0 * (nq * a->Dqk + nk * a->Dqk + (a->kv_shared ? 0.0 : nk * a->Dv) + 2.0 * nq * a->Dv);
+  const double split_s = 4.0 * a->Dqk * pairs / 1.2e15;
+  const double copy_s = 3.0 * bytes / 6.5e12 + 15e-6;
+  return split_s > copy_s;
 }
 size_t f16x_bytes(const attn_bwd_args *a) {
   if (!f16x(a)) return 0;

@@ -122,9 +122,11 @@ typedef struct {
                                        (exact for values within 2^28 of the tensor's largest
                                        magnitude, which lands just below 2^15), the fp16
                                        kernels run on the copies, and dq, dk, dv come back in
-                                       bf16 with the scales undone.  AUTO takes FP16 from
-                                       B * Sq * Hq * Dqk >= 2^22 on.  FP16 adds scaled copies
-                                       of q, k, v, o and dout to the workspace.                  */
+                                       bf16 with the scales undone.  AUTO takes FP16 when the
+                                       second products of the split form (4 Dqk flops per
+                                       attended pair) are estimated to cost more than three
+                                       passes over q, k, v, o and dout.  FP16 adds scaled
+                                       copies of q, k, v, o and dout to the workspace.          */
 } attn_bwd_args;
 
 enum { ATTN_BF16_AUTO = 0, ATTN_BF16_SPLIT = 1, ATTN_BF16_FP16 = 2 };

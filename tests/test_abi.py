@@ -186,18 +186,28 @@ def test_forward_varlen_entry_point_validates(kw, status):
 
 def test_bf16_reexpression_workspace():
     """bf16 calls computed on fp16 copies add a 1280-byte block (largest magnitudes in 4 x 64
-    slots, scales, factors) and the copies of q, k, v, o, dout; the automatic choice takes that
-    path from 2^22 elements of q on, fp16 calls never."""
+    slots, scales, factors) and the copies of q, k, v, o, dout; fp16 calls never do.  The automatic
+    choice weighs the split form's second products (4 Dqk flops per attended pair at 1.2 PFLOP/s)
+    against three passes over the inputs (at 6.5 TB/s, plus 15 us)."""
     rows = 2 * (2 * 32 * 2048 * 4)
     nq, nk = 2 * 2048 * 32 * 128, 2 * 2048 * 8 * 128
     copies = 1280 + 2 * nq + 2 * nk + 2 * nk + 2 * (2 * nq)
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=8, dtype=1, bf16_arith=2)) == rows + copies
-    assert ab.attn_bwd_workspace_size(valid_args(Hkv=8, dtype=1, bf16_arith=0)) == rows + copies  # 2^24 elements
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=8, dtype=1, bf16_arith=1)) == rows
     assert ab.attn_bwd_workspace_size(valid_args(Hkv=8, dtype=0, bf16_arith=2)) == rows
-    # below 2^22 elements of q the automatic choice keeps the bf16 products
-    small = valid_args(B=1, Sq=256, Skv=256, Hq=2, Hkv=2, dtype=1)
-    assert ab.attn_bwd_workspace_size(small) == 2 * align(2 * 256 * 4)
+
+    def auto_copies(**kw):
+        a = valid_args(dtype=1, bf16_arith=0, **kw)
+        return ab.attn_bwd_workspace_size(a) > 2 * align(a.B * a.Hq * a.Sq * 4)
+
+    # 2 x 2048 causal, 32 heads, D = 128: 134M pairs, 57 us of second products against 69 us of
+    # copies -> split; 16K-token causal GQA: 2.75 ms against 0.22 ms -> copies
+    assert not auto_copies(Hkv=8)
+    assert auto_copies(B=1, Sq=16384, Skv=16384, Hq=32, Hkv=4)
+    # a 512-key window over 8192 tokens at D = 64: 29 us against 65 us -> split
+    assert not auto_copies(B=1, Sq=8192, Skv=8192, Hq=32, Hkv=4, Dqk=64, Dv=64, window=512)
+    # small calls keep the bf16 products
+    assert not auto_copies(B=1, Sq=256, Skv=256, Hq=2, Hkv=2)
 
 
 def align(n):
