@@ -42,12 +42,15 @@ PROFILED_TRAFFIC = {
     ("dense_dkdv", "mha_causal_b2_s2048_h32_d128_fp16"): dict(
         fetch_kib=110874.9, write_kib=65536.0, fetch_scale=2.000, write_scale=1.000,
         files=("dense_dkdv.hip", "common.h"), sha="145b8d5ecab9296d"),
+    ("dense_dkdv", "gqa_causal_b1_t16384_hq32_hkv4_d128_bf16"): dict(
+        fetch_kib=6994766.6, write_kib=32768.0, fetch_scale=2.000, write_scale=1.000,
+        files=("dense_dkdv.hip", "common.h"), sha="145b8d5ecab9296d"),
     ("dense_fwd", "mha_causal_b2_s2048_h32_d128_fp16"): dict(
-        fetch_kib=74714.3, write_kib=33280.0, fetch_scale=2.000, write_scale=1.000,
-        files=("dense_fwd.hip", "common.h", "kernels.h"), sha="f6f912703952fb25"),
+        fetch_kib=78020.4, write_kib=33287.9, fetch_scale=2.000, write_scale=1.000,
+        files=("dense_fwd.hip", "common.h"), sha="6942edf4ead7cdc0"),
     ("sparse_dkdv", "sparse_mla_b1_sq4096_skv8192_h64_dqk576_dv512_top2048_bf16"): dict(
-        fetch_kib=7406762.8, write_kib=217600.0, fetch_scale=2.000, write_scale=1.000,
-        files=("sparse_dkdv.hip", "common.h"), sha="a6b6e3087a4a1667"),
+        fetch_kib=7177730.3, write_kib=217600.0, fetch_scale=2.000, write_scale=1.000,
+        files=("sparse_dkdv.hip", "common.h"), sha="a517aa98a7b03b20"),
 }
 
 
