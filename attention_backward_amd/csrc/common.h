@@ -22,6 +22,7 @@ typedef short s4v __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));  // one 32x32 f32 accumulator block
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef __bf16 b8v __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -117,6 +118,28 @@ struct F16B : F16 {
   static constexpr bool RESCALED = true;
   static __device__ __forceinline__ short cvt_out(float x) { return BF16::cvt(x); }
 };
+
+// Four values into elements e0 .. e0 + 3 (e0 a multiple of 4) of an MFMA A operand, with their
+// low halves when TT::SPLIT.  The fp16 forms convert two values per instruction into one 32-bit
+// word of the operand.
+template <class TT>
+__device__ __forceinline__ void put4(s8v &a, s8v &l, int e0, f4v x) {
+  if constexpr (TT::SPLIT) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const short xh = TT::cvt(x[i]);
+      a[e0 + i] = xh;
+      l[e0 + i] = TT::cvt(x[i] - TT::tof(xh));
+    }
+  } else {
+    typedef int i4w __attribute__((ext_vector_type(4)));
+    const h2v lo2 = {(_Float16)x[0], (_Float16)x[1]}, hi2 = {(_Float16)x[2], (_Float16)x[3]};
+    i4w w = __builtin_bit_cast(i4w, a);
+    w[e0 / 2] = __builtin_bit_cast(int, lo2);
+    w[e0 / 2 + 1] = __builtin_bit_cast(int, hi2);
+    a = __builtin_bit_cast(s8v, w);
+  }
+}
 
 // The exponent scale c and the output factors of a call: from device memory when the inputs were
 // re-expressed, else c, scale (dQ and dK) and 1 (dV).

@@ -72,9 +72,11 @@ struct DkdvLds {
 };
 
 // One work item: key block kb = item / BH of (sequence or batch, KV head, part of the head group).
-// `rotate`: the one-item-per-workgroup launch spreads packed sequences over the XCDs.
+// `rotate`: the one-item-per-workgroup launch spreads packed sequences over the XCDs.  `down`:
+// the query blocks are walked from the last one down.
 template <class TT, int D, int BN>
-__device__ __forceinline__ void dkdv_item(const Params &p, const int item, const bool rotate, DkdvLds<TT, D, BN> &L) {
+__device__ __forceinline__ void dkdv_item(const Params &p, const int item, const bool rotate, const bool down,
+                                          DkdvLds<TT, D, BN> &L) {
   using C = DkdvCfg<D, BN>;
   constexpr bool PH = DkdvLds<TT, D, BN>::PH;
   auto &q_s = L.q_s;
@@ -135,6 +137,12 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
   const int qb_lo = q_lo / BN;
   const int qb_hi = q_hi > q_lo ? (q_hi + BN - 1) / BN : qb_lo;
   const int nsteps = (qb_hi - qb_lo) * Gs;
+  // Step t covers query block step_q0(t) / BN and head h0 + t % Gs.  `down`: the walk starts at
+  // the last query block, so that the key blocks of one head running side by side (which all
+  // end their walks at the sequence's end) read the same Q/dO tiles at about the same time and
+  // share them through L2 (measured 3-6% faster on a 16K causal sequence; the work-queue launch,
+  // whose neighbours are other sequences, keeps the upward walk: 1-2% faster there).
+  auto step_q0 = [&](int t) { return (down ? qb_hi - 1 - t / Gs : qb_lo + t / Gs) * BN; };
 
   // Direct global->LDS loads of step t's Q/dO tile and of its lse/delta rows, through buffer
   // resources that start at the step's first row and head and end with the sequence: rows past
@@ -149,7 +157,7 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
   const uint32_t q_lds = lds_addr(&q_s[0][0]), do_lds = lds_addr(&do_s[0][0]);
   const uint32_t row_lds = lds_addr(w == 0 ? &lse_s[0][0] : &dl_s[0][0]);
   auto issue = [&](int t, int qbuf, int buf) {
-    const int q0 = (qb_lo + t / Gs) * BN;
+    const int q0 = step_q0(t);
     const int h = h0 + t % Gs;
     const int64_t e0 = ((sv.q0 + q0) * p.Hq + h) * D;  // element (row q0, head h)
     const uint64_t nbytes = ((uint64_t)(Sq - q0) * p.Hq - h) * D * 2;
@@ -193,10 +201,9 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
   // A operands of phase 2, P^T or dS^T, A[m=key][k=query], with their low halves when
   // TT::SPLIT: register 8*(ks%2)+e of block ks/2 is query 16*ks + 8*(e/4) + 4*hi + e%4, which
   // matches the rows the transposed read of the B operand supplies.
-  auto pack = [&](s8v *pa, s8v *pl, int mb, int r, float x) {
-    const short xh = TT::cvt(x);
-    pa[2 * mb + (r >> 3)][r & 7] = xh;
-    pl[2 * mb + (r >> 3)][r & 7] = TT::SPLIT ? TT::cvt(x - TT::tof(xh)) : (short)0;
+  // Registers 4 j .. 4 j + 3 of block mb.
+  auto pack4 = [&](s8v *pa, s8v *pl, int mb, int j, f4v x) {
+    put4<TT>(pa[2 * mb + (j >> 1)], pl[2 * mb + (j >> 1)], 4 * (j & 1), x);
   };
   // acc += A^T B with B[k=query][n=d] read transposed from the row-major tile `src`.  The LDS
   // operands are read PF products ahead through a ring of registers, so that the read latency
@@ -253,7 +260,6 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
     }
   };
   const Factors fac = factors(p);
-  auto step_q0 = [&](int t) { return (qb_lo + t / Gs) * BN; };
   auto step_full = [&](int q0) {
     return (!p.causal || k0 + C::BM - 1 <= q0 + off) && (p.window <= 0 || k0 > q0 + BN - 1 + off - p.window) &&
            (q0 + BN <= Sq) && (k0 + C::BM <= Skv);
@@ -288,8 +294,8 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
                 x = ((qi >= qlo) & (qi <= qhi)) ? x : 0.f;
               }
               pq[i] = x;
-              pack(pa, pl, mb, 4 * j + i, x);
             }
+            pack4(pa, pl, mb, j, pq);
             if (!PH) p_s[kgrp][mb][j][lane] = pq;
           }
         }
@@ -330,15 +336,18 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
       for (int mb = 0; mb < C::MB; mb++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
+          f4v pq;
           if (PH) {
             const s8v ph = ph_s[kgrp][2 * mb + (j >> 1)][lane];
 #pragma unroll
-            for (int i = 0; i < 4; i++) pack(da, dl, mb, 4 * j + i, ds_of<TT>(TT::tof(ph[4 * (j & 1) + i]), s[mb][4 * j + i], fac));
+            for (int i = 0; i < 4; i++) pq[i] = TT::tof(ph[4 * (j & 1) + i]);
           } else {
-            const f4v pq = p_s[kgrp][mb][j][lane];
-#pragma unroll
-            for (int i = 0; i < 4; i++) pack(da, dl, mb, 4 * j + i, ds_of<TT>(pq[i], s[mb][4 * j + i], fac));
+            pq = p_s[kgrp][mb][j][lane];
           }
+          f4v dsv;
+#pragma unroll
+          for (int i = 0; i < 4; i++) dsv[i] = ds_of<TT>(pq[i], s[mb][4 * j + i], fac);
+          pack4(da, dl, mb, j, dsv);
         }
       wait_vm0();
       __syncthreads();  // next tile landed; P consumed
@@ -378,7 +387,7 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
 template <class TT, int D, int BN>
 __global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
   __shared__ DkdvLds<TT, D, BN> L;
-  dkdv_item<TT, D, BN>(p, blockIdx.x, true, L);
+  dkdv_item<TT, D, BN>(p, blockIdx.x, true, true, L);
 }
 
 // Work-queue form: one workgroup per CU takes items in index order (key blocks longest first)
@@ -395,7 +404,7 @@ __global__ __launch_bounds__(512, 1) void dense_dkdv_queue_kernel(const Params p
     const int u = next;
     __syncthreads();
     if (u < 0 || u >= nitems) break;
-    dkdv_item<TT, D, BN>(p, u, false, L);
+    dkdv_item<TT, D, BN>(p, u, false, false, L);
   }
 }
 

@@ -238,16 +238,19 @@ __global__ __launch_bounds__(512, 1) void dense_dq_kernel(const Params p) {
 #pragma unroll
           for (int kb = 0; kb < KBS; kb++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-              float x = exp2f_hw(s[kb][r] * fac.c - lr);
-              if (decltype(masked)::value) {
-                const int kj = k0 + 32 * (sb * KBS + kb) + 8 * (r >> 2) + 4 * hi + (r & 3);
-                x = ((kj >= klo) & (kj <= khi)) ? x : 0.f;
+            for (int j = 0; j < 4; j++) {
+              f4v ds;
+#pragma unroll
+              for (int i = 0; i < 4; i++) {
+                const int r = 4 * j + i;
+                float x = exp2f_hw(s[kb][r] * fac.c - lr);
+                if (decltype(masked)::value) {
+                  const int kj = k0 + 32 * (sb * KBS + kb) + 8 * j + 4 * hi + i;
+                  x = ((kj >= klo) & (kj <= khi)) ? x : 0.f;
+                }
+                ds[i] = ds_of<TT>(x, dp[kb][r], fac);
               }
-              const float ds = ds_of<TT>(x, dp[kb][r], fac);
-              const short dh = TT::cvt(ds);
-              da[2 * kb + (r >> 3)][r & 7] = dh;
-              dl[2 * kb + (r >> 3)][r & 7] = TT::SPLIT ? TT::cvt(ds - TT::tof(dh)) : (short)0;
+              put4<TT>(da[2 * kb + (j >> 1)], dl[2 * kb + (j >> 1)], 4 * (j & 1), ds);
             }
         };
         if (full)
