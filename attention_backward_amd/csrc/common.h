@@ -272,6 +272,16 @@ __device__ __forceinline__ void b2lds4_at(i4v r, uint32_t voff, uint32_t lds_byt
                : "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "v"(voff), "s"(r)
                : "memory", "m0");
 }
+// A 16-byte load into registers through a buffer resource over `bytes` bytes from `base`:
+// offsets past the end read as zero, with no select on the loaded value (which would keep the
+// load's destination registers apart from the variable they end in).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc_v(const void *base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ s8v buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(s8v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 // Wait for every outstanding vector-memory operation (vmcnt = 0; expcnt and lgkmcnt left at their
 // no-wait maxima in the gfx9 encoding).  Issued through the builtin so that the compiler's own
 // wait placement knows the loads it issued itself are complete from here on.

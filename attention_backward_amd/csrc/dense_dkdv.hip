@@ -18,13 +18,16 @@
 //   waves 4..7 ("dS role") own the same four key groups: hold V rows, form dP = dO V^T, read
 //                          P, form dS = P (dP - delta) and accumulate dK += dS^T Q.
 // Each wave keeps one resident operand and one accumulator, so everything fits in 256 VGPRs
-// (no AGPR traffic) and two waves share each SIMD.  P crosses in f32 so dS is formed from
-// unrounded P and rounded once (bf16: P and dS enter their products as hi + lo halves).
+// (no AGPR traffic) and two waves share each SIMD.  P crosses as the fp16 operand of the dV
+// product; in the bf16 split form it crosses in f32, so dS is formed from unrounded P and
+// rounded once (P and dS then enter their products as hi + lo halves).
 // Q/dO tiles (BN query rows of one head) are double-buffered in LDS and filled by direct
 // global->LDS loads into unpadded, XOR-swizzled rows; lse and delta rows come the same way.
-// P^T and dS^T are formed in the accumulator layout and fed to the next product as A operands
-// directly; dO and Q enter that product transposed through ds_read_tr16_b64.  Causal / window
-// tiles entirely outside the mask are never visited; tiles fully inside it skip the mask.
+// P and dS are formed in the accumulator layout and fed to the next product as B operands
+// directly; dO and Q enter that product transposed through ds_read_tr16_b64, which leaves dV^T
+// and dK^T in the accumulators.  Causal / window tiles entirely outside the mask are never
+// visited; tiles fully inside it skip the mask.  At D = 128 a workgroup per CU runs a fixed
+// sequence of items, loading the next item's first tile during the current item's last step.
 #include <type_traits>
 
 #include <algorithm>
@@ -52,6 +55,10 @@ struct DkdvCfg {
   static_assert(BN <= 64, "lse/delta rows are loaded by one wave instruction each");
 };
 
+#ifndef ATTN_DKDV_SEQ
+#define ATTN_DKDV_SEQ 1
+#endif
+
 #ifndef ATTN_P_HALF
 #define ATTN_P_HALF 1
 #endif
@@ -71,12 +78,61 @@ struct DkdvLds {
   s8v ph_s[PH ? 4 : 1][BN / 16][64];    // element-type P: [key group][k-step][lane]
 };
 
-// One work item: key block kb = item / BH of (sequence or batch, KV head, part of the head group).
-// `rotate`: the one-item-per-workgroup launch spreads packed sequences over the XCDs.  `down`:
-// the query blocks are walked from the last one down.
-template <class TT, int D, int BN>
-__device__ __forceinline__ void dkdv_item(const Params &p, const int item, const bool rotate, const bool down,
-                                          DkdvLds<TT, D, BN> &L) {
+// Geometry of one work item, uniform over the workgroup: key block kb = item / BH of (sequence or
+// batch, KV head, part of the head group).  `rotate`: the one-workgroup-per-item order spreads
+// packed sequences over the XCDs.
+struct DkdvItem {
+  int sp, g, h0, Gs, k0, Sq, Skv, off, qb_lo, qb_hi, nsteps;
+  bool live;  // false: the key block starts past the end of its sequence (nothing to store)
+  SeqView sv;
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ DkdvItem dkdv_geo(const Params &p, const int item, const bool rotate) {
+  DkdvItem it;
+  // hsplit items share a key block: part sp walks query heads [sp * Gs, (sp + 1) * Gs) of the KV
+  // head's group and stores its finished f32 block into its own slice.
+  const int BH = (p.cu ? p.nseq : p.B) * p.Hkv * p.hsplit;
+  const int kb = item / BH;
+  // Packed sequences without a window: rotate the (sequence, head) index by the key block.
+  // Workgroups go round-robin over the 8 XCDs, so with (sequences x heads) a multiple of 8 every
+  // block of one sequence would land on the same few XCDs, and one long sequence would leave the
+  // rest idle (measured 3.4x slower).  Under a window, neighbouring key blocks share most of their
+  // query rows and the plain order keeps more of them in one L2 (measured 25% faster).
+  const int rot = rotate && p.cu && p.window == 0 ? kb : 0;
+  const int bgs = (item % BH + rot) % BH;
+  const int bg = bgs / p.hsplit;
+  it.sp = bgs % p.hsplit;
+  it.Gs = p.G / p.hsplit;
+  it.g = bg % p.Hkv;
+  it.h0 = it.g * p.G + it.sp * it.Gs;
+  it.k0 = kb * BM;
+  it.sv = seq_view(p.cu, bg / p.Hkv, p.Sq, p.Skv, p.Hq, p.max_seqlen);
+  it.Sq = it.sv.Sq;
+  it.Skv = it.sv.Skv;
+  it.off = it.Skv - it.Sq;
+  it.live = it.k0 < it.Skv;
+  // Query rows that can see some key of this block.
+  int q_lo = 0, q_hi = it.Sq;
+  if (p.causal) q_lo = max(0, it.k0 - it.off);
+  if (p.window > 0) q_hi = min(it.Sq, it.k0 + BM - 1 - it.off + p.window);
+  it.qb_lo = q_lo / BN;
+  it.qb_hi = q_hi > q_lo ? (q_hi + BN - 1) / BN : it.qb_lo;
+  it.nsteps = it.live ? (it.qb_hi - it.qb_lo) * it.Gs : 0;
+  return it;
+}
+
+// How a workgroup gets its items: one item per workgroup; a fixed sequence known in advance
+// (the next item's first Q/dO tile then goes out at the start of the current item's last step,
+// in flight during that step and the epilogue); or drawn from the work queue after each item.
+enum { DKDV_ONE = 0, DKDV_SEQ = 1, DKDV_QUEUE = 2 };
+
+// A workgroup runs the items item, next(item), next(next(item)), ... while they are below
+// nitems; each next item's K/V rows are loaded after the current item's epilogue.  `down`: the
+// query blocks are walked from the last one.
+template <class TT, int D, int BN, int MODE, class Next>
+__device__ __forceinline__ void dkdv_run(const Params &p, int item, const int nitems, Next next, const bool rotate,
+                                         const bool down, DkdvLds<TT, D, BN> &L) {
   using C = DkdvCfg<D, BN>;
   constexpr bool PH = DkdvLds<TT, D, BN>::PH;
   auto &q_s = L.q_s;
@@ -91,63 +147,22 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
   const int role = w >> 2, kgrp = w & 3;
   const int hi = lane >> 5, lo = lane & 31;
   const int i16 = lane & 15, g16 = lane >> 4;
-  // hsplit items share a key block: part sp walks query heads [sp * Gs, (sp + 1) * Gs) of the KV
-  // head's group and stores its finished f32 block into its own slice.
-  const int BH = (p.cu ? p.nseq : p.B) * p.Hkv * p.hsplit;
-  const int kb = item / BH;
-  // Packed sequences without a window: rotate the (sequence, head) index by the key block.
-  // Workgroups go round-robin over the 8 XCDs, so with (sequences x heads) a multiple of 8 every
-  // block of one sequence would land on the same few XCDs, and one long sequence would leave the
-  // rest idle (measured 3.4x slower).  Under a window, neighbouring key blocks share most of their
-  // query rows and the plain order keeps more of them in one L2 (measured 25% faster).
-  const int rot = rotate && p.cu && p.window == 0 ? kb : 0;
-  const int bgs = (item % BH + rot) % BH;
-  const int bg = bgs / p.hsplit, sp = bgs % p.hsplit;
-  const int Gs = p.G / p.hsplit;
-  const int b = bg / p.Hkv, g = bg % p.Hkv, h0 = g * p.G + sp * Gs;
-  const int k0 = kb * C::BM;
-  const SeqView sv = seq_view(p.cu, b, p.Sq, p.Skv, p.Hq, p.max_seqlen);
-  const int Sq = sv.Sq, Skv = sv.Skv;
-  if (k0 >= Skv) return;  // a packed sequence shorter than the longest (whole workgroup)
-  const int kbase = k0 + 32 * kgrp;
-  const int off = Skv - Sq;
 
-  // This wave's 32 K rows (P role) or V rows (dS role) as MFMA B operands B[k=d][n=key], and
-  // the range [qlo, qhi] of query rows allowed to see the lane's key.
-  s8v kv[C::KK];
-  const int kj = kbase + lo;
-  {
-    const bool ok = kj < Skv;
-    const short *row = (role == 0 ? p.k : p.v) + ((sv.k0 + (ok ? kj : 0)) * p.Hkv + g) * D + 8 * hi;
-#pragma unroll
-    for (int kk = 0; kk < C::KK; kk++) kv[kk] = ok ? *(const s8v *)(row + 16 * kk) : s8v{};
-  }
-  int qlo = p.causal ? kj - off : 0;
-  int qhi = p.window > 0 ? min(Sq - 1, kj - off + p.window - 1) : Sq - 1;
-  if (kj >= Skv) qhi = qlo - 1;
+  // Step t of an item covers query block step_q0(t) / BN and head h0 + t % Gs.  With `down` the
+  // walk starts at the last query block, so that the key blocks of one head running side by side
+  // (which all end their walks at the sequence's end) read the same Q/dO tiles at about the same
+  // time and share them through L2 (measured 3-6% faster on a 16K causal sequence; the
+  // work-queue launch, whose neighbours are other sequences, keeps the upward walk: 1-2% faster
+  // there).
+  auto step_q0 = [&](const DkdvItem &it, int t) {
+    return (down ? it.qb_hi - 1 - t / it.Gs : it.qb_lo + t / it.Gs) * BN;
+  };
 
-  f16v acc[C::ND];  // P role: dV, dS role: dK; [32-wide d block], rows = this wave's 32 keys
-#pragma unroll
-  for (int dn = 0; dn < C::ND; dn++) acc[dn] = f16v{};
-
-  // Query rows that can see some key of this block.
-  int q_lo = 0, q_hi = Sq;
-  if (p.causal) q_lo = max(0, k0 - off);
-  if (p.window > 0) q_hi = min(Sq, k0 + C::BM - 1 - off + p.window);
-  const int qb_lo = q_lo / BN;
-  const int qb_hi = q_hi > q_lo ? (q_hi + BN - 1) / BN : qb_lo;
-  const int nsteps = (qb_hi - qb_lo) * Gs;
-  // Step t covers query block step_q0(t) / BN and head h0 + t % Gs.  `down`: the walk starts at
-  // the last query block, so that the key blocks of one head running side by side (which all
-  // end their walks at the sequence's end) read the same Q/dO tiles at about the same time and
-  // share them through L2 (measured 3-6% faster on a 16K causal sequence; the work-queue launch,
-  // whose neighbours are other sequences, keeps the upward walk: 1-2% faster there).
-  auto step_q0 = [&](int t) { return (down ? qb_hi - 1 - t / Gs : qb_lo + t / Gs) * BN; };
-
-  // Direct global->LDS loads of step t's Q/dO tile and of its lse/delta rows, through buffer
+  // Direct global->LDS loads of a step's Q/dO tile and of its lse/delta rows, through buffer
   // resources that start at the step's first row and head and end with the sequence: rows past
   // Sq read as zero (the mask zeroes their scores).  The lanes' byte offsets within a tile are
-  // computed once; a step only forms its resources (scalar work).
+  // computed once; a step only forms its resources (scalar work).  Step t of item `it` lands in
+  // the buffers of the workgroup's running step count T: q_s[T % 3], do_s[T % 2].
   uint32_t ld_off[C::WIW];
 #pragma unroll
   for (int u = 0; u < C::WIW; u++) {
@@ -156,11 +171,12 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
   }
   const uint32_t q_lds = lds_addr(&q_s[0][0]), do_lds = lds_addr(&do_s[0][0]);
   const uint32_t row_lds = lds_addr(w == 0 ? &lse_s[0][0] : &dl_s[0][0]);
-  auto issue = [&](int t, int qbuf, int buf) {
-    const int q0 = step_q0(t);
-    const int h = h0 + t % Gs;
-    const int64_t e0 = ((sv.q0 + q0) * p.Hq + h) * D;  // element (row q0, head h)
-    const uint64_t nbytes = ((uint64_t)(Sq - q0) * p.Hq - h) * D * 2;
+  auto issue = [&](const DkdvItem &it, int t, int T) {
+    const int qbuf = T % 3, buf = T & 1;
+    const int q0 = step_q0(it, t);
+    const int h = it.h0 + t % it.Gs;
+    const int64_t e0 = ((it.sv.q0 + q0) * p.Hq + h) * D;  // element (row q0, head h)
+    const uint64_t nbytes = ((uint64_t)(it.Sq - q0) * p.Hq - h) * D * 2;
     const i4v rq = buf_rsrc(p.q + e0, nbytes), rd = buf_rsrc(p.dout + e0, nbytes);
 #pragma unroll
     for (int u = 0; u < C::WIW; u++) {
@@ -169,11 +185,26 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
       b2lds16_at(rd, ld_off[u], do_lds + 2 * buf * BN * D + slot_b);
     }
     if (w < 2) {
-      const int64_t li = sv.l0 + (int64_t)h * p.Sq + q0;
-      const i4v rl = buf_rsrc((w == 0 ? p.lse : p.ndelta) + li, (uint64_t)(Sq - q0) * 4);
+      const int64_t li = it.sv.l0 + (int64_t)h * p.Sq + q0;
+      const i4v rl = buf_rsrc((w == 0 ? p.lse : p.ndelta) + li, (uint64_t)(it.Sq - q0) * 4);
       b2lds4_at(rl, (uint32_t)min(lane, BN - 1) * 4, row_lds + 4 * 64 * buf);
     }
   };
+
+  // This wave's 32 K rows (P role) or V rows (dS role) of an item as MFMA B operands
+  // B[k=d][n=key] (rows past the sequence read as zero).
+  s8v kv[C::KK];
+  auto load_kv = [&](const DkdvItem &it) {
+    // The resource starts at row k0, head g and ends with the sequence (nothing when the block
+    // starts past it).
+    const short *base = (role == 0 ? p.k : p.v) + ((int64_t)(it.sv.k0 + it.k0) * p.Hkv + it.g) * D;
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc_v(base, ((int64_t)(it.Skv - it.k0) * p.Hkv - it.g) * D * 2);
+    const uint32_t off = (uint32_t)(((32 * kgrp + lo) * p.Hkv * D + 8 * hi) * 2);
+#pragma unroll
+    for (int kk = 0; kk < C::KK; kk++) kv[kk] = buf_load16(r, off + 32 * kk);
+  };
+
+  f16v acc[C::ND];  // P role: dV^T, dS role: dK^T; [32-wide d block], columns = this wave's keys
 
   // Per-lane LDS offsets (elements): natural read of query row 32*mb + lo, logical chunk
   // 2*kk + hi; transposed read of rows 16*ks + 8*half + 4*hi + i16/4, columns 32*dn +
@@ -190,24 +221,25 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
 
   // The two roles run separate copies of the step loop (same trip count, same barriers), so that
   // registers live in one role's loop are not reserved in the other's.
-  //   P role:  S = Q K^T; P = exp2(S c - lse) masked -> LDS (f32) and A operands; | barrier |
-  //            dV += P^T dO; | barrier |
-  //   dS role: dK += dS^T Q of the previous step; dP = dO V^T; | barrier | dS = P (dP - delta)
+  //   P role:  S = Q K^T; P = exp2(S c - lse) masked -> LDS and B operands; | barrier |
+  //            dV^T += dO^T P; | barrier |
+  //   dS role: dK^T += Q^T dS of the previous step; dP = dO V^T; | barrier | dS = P (dP - delta)
   //            from the partner's P; | barrier |
   // The dS role applies dK one step late (dS kept in registers, Q of step t-1 in the third Q
   // buffer), so it keeps the matrix core busy while its P-role partner on the same SIMD works
   // through the softmax.
   //
-  // A operands of phase 2, P^T or dS^T, A[m=key][k=query], with their low halves when
-  // TT::SPLIT: register 8*(ks%2)+e of block ks/2 is query 16*ks + 8*(e/4) + 4*hi + e%4, which
-  // matches the rows the transposed read of the B operand supplies.
+  // B operands of phase 2, P or dS, B[k=query][n=key], with their low halves when TT::SPLIT:
+  // register 8*(ks%2)+e of block ks/2 is query 16*ks + 8*(e/4) + 4*hi + e%4, which matches the
+  // columns the transposed read of the A operand supplies.
   // Registers 4 j .. 4 j + 3 of block mb.
   auto pack4 = [&](s8v *pa, s8v *pl, int mb, int j, f4v x) {
     put4<TT>(pa[2 * mb + (j >> 1)], pl[2 * mb + (j >> 1)], 4 * (j & 1), x);
   };
-  // acc += A^T B with B[k=query][n=d] read transposed from the row-major tile `src`.  The LDS
-  // operands are read PF products ahead through a ring of registers, so that the read latency
-  // hides behind the matrix core instead of stalling it before every product.
+  // acc += A B with A[m=d][k=query] read transposed from the row-major tile `src`: acc holds
+  // dV^T or dK^T (rows d, columns this wave's keys).  The LDS operands are read PF products ahead
+  // through a ring of registers, so that the read latency hides behind the matrix core instead
+  // of stalling it before every product.
   // Per-lane byte offsets of both reads within a tile; the step's tile base is added once per
   // offset and the row-block offsets fold into the read instructions.
   uint32_t tr_lane[C::ND][2], nat_lane[C::KK];
@@ -236,8 +268,8 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
       if (n + PF < N) ring[(n + PF) % (PF + 1)] = ld(n + PF);
       sched_fence();
       const int ks = n / C::ND, dn = n % C::ND;
-      acc[dn] = TT::mfma(pa[ks], ring[n % (PF + 1)], acc[dn]);
-      if (TT::SPLIT) acc[dn] = TT::mfma(pl[ks], ring[n % (PF + 1)], acc[dn]);
+      acc[dn] = TT::mfma(ring[n % (PF + 1)], pa[ks], acc[dn]);
+      if (TT::SPLIT) acc[dn] = TT::mfma(ring[n % (PF + 1)], pl[ks], acc[dn]);
     }
   };
   // Phase 1 for M = the step's queries, N = this wave's keys, A rows from `src` (same ring).
@@ -260,152 +292,236 @@ __device__ __forceinline__ void dkdv_item(const Params &p, const int item, const
     }
   };
   const Factors fac = factors(p);
-  auto step_full = [&](int q0) {
-    return (!p.causal || k0 + C::BM - 1 <= q0 + off) && (p.window <= 0 || k0 > q0 + BN - 1 + off - p.window) &&
-           (q0 + BN <= Sq) && (k0 + C::BM <= Skv);
-  };
 
-  if (nsteps > 0) issue(0, 0, 0);
+  DkdvItem cur = dkdv_geo<C::BM, BN>(p, item, rotate);
+  load_kv(cur);
+  int T = 0;  // steps run so far: buffer parity across items
+  if (cur.nsteps > 0) issue(cur, 0, 0);
   wait_vm0();
   __syncthreads();
 
-  if (role == 0) {
-    for (int t = 0; t < nsteps; t++) {
-      const int buf = t & 1;
-      const int q0 = step_q0(t);
-      if (t + 1 < nsteps) issue(t + 1, (t + 1) % 3, buf ^ 1);
-      f16v s[C::MB] = {};
-      mfma_prio_hi();
-      phase1(s, q_s[t % 3]);
-      mfma_prio_lo();
-      s8v pa[C::KS], pl[C::KS];
-      auto softmax = [&](auto masked) {
+  for (;;) {
+    const int nitem = MODE == DKDV_SEQ ? next(item) : nitems;
+    const bool has_next = nitem < nitems;  // known in advance (DKDV_SEQ only)
+    const int n = cur.nsteps;
+    const int kbase = cur.k0 + 32 * kgrp;
+    // The range [qlo, qhi] of query rows allowed to see the lane's key.
+    const int kj = kbase + lo;
+    const int qlo = p.causal ? kj - cur.off : 0;
+    const int qhi = kj >= cur.Skv ? qlo - 1
+                    : p.window > 0 ? min(cur.Sq - 1, kj - cur.off + p.window - 1)
+                                   : cur.Sq - 1;
+    auto step_full = [&](int q0) {
+      return (!p.causal || cur.k0 + C::BM - 1 <= q0 + cur.off) &&
+             (p.window <= 0 || cur.k0 > q0 + BN - 1 + cur.off - p.window) && (q0 + BN <= cur.Sq) &&
+             (cur.k0 + C::BM <= cur.Skv);
+    };
+    // The loads of step t + 1: the item's own next step, or at its last step the next item's
+    // first.  A step ends by waiting for them, except the last, which leaves the next item's
+    // tile in flight.
+    auto issue_next = [&](int t) {
+      if (t + 1 < n) {
+        issue(cur, t + 1, T + t + 1);
+      } else if (has_next) {
+        const DkdvItem nx = dkdv_geo<C::BM, BN>(p, nitem, rotate);
+        if (nx.nsteps > 0) issue(nx, 0, T + t + 1);
+      }
+    };
+    auto end_step = [&](int t) {
+      if (t + 1 < n) wait_vm0();
+      __syncthreads();
+    };
 #pragma unroll
-        for (int mb = 0; mb < C::MB; mb++) {
+    for (int dn = 0; dn < C::ND; dn++) acc[dn] = f16v{};
+
+    if (role == 0) {
+      for (int t = 0; t < n; t++) {
+        const int buf = (T + t) & 1;
+        const int q0 = step_q0(cur, t);
+        issue_next(t);
+        f16v s[C::MB] = {};
+        mfma_prio_hi();
+        phase1(s, q_s[(T + t) % 3]);
+        mfma_prio_lo();
+        s8v pa[C::KS], pl[C::KS];
+        auto softmax = [&](auto masked) {
+#pragma unroll
+          for (int mb = 0; mb < C::MB; mb++) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+              const f4v l4 = *(const f4v *)&lse_s[buf][32 * mb + 8 * j + 4 * hi];
+              f4v pq;
+#pragma unroll
+              for (int i = 0; i < 4; i++) {
+                float x = exp2f_hw(s[mb][4 * j + i] * fac.c - l4[i]);
+                if (decltype(masked)::value) {
+                  const int qi = q0 + 32 * mb + 8 * j + 4 * hi + i;
+                  x = ((qi >= qlo) & (qi <= qhi)) ? x : 0.f;
+                }
+                pq[i] = x;
+              }
+              pack4(pa, pl, mb, j, pq);
+              if (!PH) p_s[kgrp][mb][j][lane] = pq;
+            }
+          }
+        };
+        if (step_full(q0))
+          softmax(std::false_type{});
+        else
+          softmax(std::true_type{});
+        if (PH) {
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ks++) ph_s[kgrp][ks][lane] = pa[ks];
+        }
+        __syncthreads();  // P visible to the dS-role waves
+        phase2(pa, pl, do_s[buf]);  // dV^T += dO^T P
+        end_step(t);  // next tile landed; P and this step's dO consumed
+      }
+    } else {
+      s8v da[C::KS], dl[C::KS];  // dS of the previous step (B operands)
+      for (int t = 0; t < n; t++) {
+        const int buf = (T + t) & 1;
+        issue_next(t);
+        if (t > 0) phase2(da, dl, q_s[(T + t + 2) % 3]);  // dK^T += Q^T dS of step t-1
+        // dP accumulators start from minus delta of their query rows (register 4 j + i of block
+        // mb is row 32 mb + 8 j + 4 hi + i), so the products leave dP - delta in them.
+        f16v s[C::MB];
+#pragma unroll
+        for (int mb = 0; mb < C::MB; mb++)
 #pragma unroll
           for (int j = 0; j < 4; j++) {
-            const f4v l4 = *(const f4v *)&lse_s[buf][32 * mb + 8 * j + 4 * hi];
+            const f4v d4 = *(const f4v *)&dl_s[buf][32 * mb + 8 * j + 4 * hi];
+#pragma unroll
+            for (int i = 0; i < 4; i++) s[mb][4 * j + i] = d4[i];
+          }
+        phase1(s, do_s[buf]);  // dP - delta = dO V^T - delta
+        __syncthreads();  // P of this step visible
+#pragma unroll
+        for (int mb = 0; mb < C::MB; mb++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
             f4v pq;
+            if (PH) {
+              const s8v ph = ph_s[kgrp][2 * mb + (j >> 1)][lane];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-              float x = exp2f_hw(s[mb][4 * j + i] * fac.c - l4[i]);
-              if (decltype(masked)::value) {
-                const int qi = q0 + 32 * mb + 8 * j + 4 * hi + i;
-                x = ((qi >= qlo) & (qi <= qhi)) ? x : 0.f;
-              }
-              pq[i] = x;
+              for (int i = 0; i < 4; i++) pq[i] = TT::tof(ph[4 * (j & 1) + i]);
+            } else {
+              pq = p_s[kgrp][mb][j][lane];
             }
-            pack4(pa, pl, mb, j, pq);
-            if (!PH) p_s[kgrp][mb][j][lane] = pq;
-          }
-        }
-      };
-      if (step_full(q0))
-        softmax(std::false_type{});
-      else
-        softmax(std::true_type{});
-      if (PH) {
+            f4v dsv;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ks++) ph_s[kgrp][ks][lane] = pa[ks];
+            for (int i = 0; i < 4; i++) dsv[i] = ds_of<TT>(pq[i], s[mb][4 * j + i], fac);
+            pack4(da, dl, mb, j, dsv);
+          }
+        end_step(t);  // next tile landed; P consumed
       }
-      __syncthreads();  // P visible to the dS-role waves
-      phase2(pa, pl, do_s[buf]);  // dV += P^T dO
-      wait_vm0();
-      __syncthreads();  // next tile landed; P and this step's dO consumed
+      if (n > 0) phase2(da, dl, q_s[(T + n - 1) % 3]);
     }
-  } else {
-    s8v da[C::KS], dl[C::KS];  // dS^T of the previous step
-    for (int t = 0; t < nsteps; t++) {
-      const int buf = t & 1;
-      if (t + 1 < nsteps) issue(t + 1, (t + 1) % 3, buf ^ 1);
-      if (t > 0) phase2(da, dl, q_s[(t + 2) % 3]);  // dK += dS^T Q of step t-1
-      // dP accumulators start from minus delta of their query rows (register 4 j + i of block mb
-      // is row 32 mb + 8 j + 4 hi + i), so the products leave dP - delta in them.
-      f16v s[C::MB];
-#pragma unroll
-      for (int mb = 0; mb < C::MB; mb++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const f4v d4 = *(const f4v *)&dl_s[buf][32 * mb + 8 * j + 4 * hi];
-#pragma unroll
-          for (int i = 0; i < 4; i++) s[mb][4 * j + i] = d4[i];
-        }
-      phase1(s, do_s[buf]);  // dP - delta = dO V^T - delta
-      __syncthreads();       // P of this step visible
-#pragma unroll
-      for (int mb = 0; mb < C::MB; mb++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          f4v pq;
-          if (PH) {
-            const s8v ph = ph_s[kgrp][2 * mb + (j >> 1)][lane];
-#pragma unroll
-            for (int i = 0; i < 4; i++) pq[i] = TT::tof(ph[4 * (j & 1) + i]);
-          } else {
-            pq = p_s[kgrp][mb][j][lane];
-          }
-          f4v dsv;
-#pragma unroll
-          for (int i = 0; i < 4; i++) dsv[i] = ds_of<TT>(pq[i], s[mb][4 * j + i], fac);
-          pack4(da, dl, mb, j, dsv);
-        }
-      wait_vm0();
-      __syncthreads();  // next tile landed; P consumed
-    }
-    if (nsteps > 0) phase2(da, dl, q_s[(nsteps - 1) % 3]);
-  }
 
-  // Epilogue: dV (P role) or scale * dK (dS role), cast once, BSHD at the KV head.
-  const float sc = role == 0 ? fac.dv : fac.dk;
-  if (p.hsplit > 1) {
-    // Part sp of the head group stores its unscaled f32 block with plain stores into its own
-    // slice [sp][tokens, Hkv, D]; the landing pass adds the slices in a fixed order.
-    float *acc_out = (role == 0 ? p.dv_acc : p.dk_acc) + (int64_t)sp * p.acc_slice;
+    // Epilogue: dV (P role) or scale * dK (dS role), cast once, BSHD at the KV head.  The
+    // accumulators hold the transposes: register 4 j + i of block dn is column d = 32 dn + 8 j +
+    // 4 hi + i of key kbase + lo.
+    if (p.hsplit > 1) {
+      // Part sp of the head group stores its unscaled f32 block with plain stores into its own
+      // slice [sp][tokens, Hkv, D]; the landing pass adds the slices in a fixed order.
+      if (cur.live && kj < cur.Skv) {
+        float *row = (role == 0 ? p.dv_acc : p.dk_acc) + (int64_t)cur.sp * p.acc_slice +
+                     ((cur.sv.k0 + kj) * p.Hkv + cur.g) * D + 4 * hi;
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int key = kbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (key < Skv) {
-        float *row = acc_out + ((sv.k0 + key) * p.Hkv + g) * D + lo;
+        for (int dn = 0; dn < C::ND; dn++)
 #pragma unroll
-        for (int dn = 0; dn < C::ND; dn++) row[32 * dn] = acc[dn][r];
+          for (int j = 0; j < 4; j++)
+            *(f4v *)(row + 32 * dn + 8 * j) = f4v{acc[dn][4 * j], acc[dn][4 * j + 1], acc[dn][4 * j + 2], acc[dn][4 * j + 3]};
+      }
+    } else {
+      // The wave's 32 x D block goes through LDS so that the global stores are whole rows (16
+      // lanes x 16 bytes per 256-byte row): staged row-major, 16-byte chunk c of row r at chunk
+      // c ^ (r mod CPR).  Staging space, 32 D 2 bytes per wave, two waves per buffer: the two Q
+      // buffers and the dO buffer not holding the next item's first tile, and the P exchange.
+      __syncthreads();  // the dS role's last product has read its Q buffer
+      const float sc = role == 0 ? fac.dv : fac.dk;
+      constexpr int WB = 32 * D * 2;  // bytes per wave
+      static_assert(2 * WB <= (int)sizeof(q_s[0]) && 2 * WB <= (int)sizeof(p_s) + (int)sizeof(ph_s),
+                    "staging space");
+      const int rg = w >> 1;
+      const uint32_t stg = (rg == 0   ? lds_addr(&q_s[(T + n + 2) % 3][0])
+                            : rg == 1 ? lds_addr(&q_s[(T + n + 1) % 3][0])
+                            : rg == 2 ? lds_addr(&do_s[(T + n + 1) & 1][0])
+                                      : (PH ? lds_addr(&ph_s[0][0][0]) : lds_addr(&p_s[0][0][0][0]))) +
+                           (w & 1) * WB;
+      // Lane terms recomputed here (opaque) rather than hoisted out of the item loop, where they
+      // would hold registers through every step.
+      const int ln = (int)opaque((uint32_t)lane), lo_e = ln & 31, swl = lo_e & (C::CPR - 1);
+      const uint32_t wr = stg + lo_e * D * 2 + 8 * (ln >> 5);
+#pragma unroll
+      for (int dn = 0; dn < C::ND; dn++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          s4v o;
+#pragma unroll
+          for (int i = 0; i < 4; i++) o[i] = TT::cvt_out(acc[dn][4 * j + i] * sc);
+          const int c = 4 * dn + j;
+          *(__attribute__((address_space(3))) s4v *)(size_t)(wr + ((c ^ swl) * 16)) = o;
+        }
+      if (cur.live) {
+        constexpr int RPI = 64 / C::CPR;  // rows per store instruction
+        const int c = ln % C::CPR;
+        short *dst = (role == 0 ? p.dv : p.dk) + (int64_t)cur.g * D + 8 * c;
+#pragma unroll
+        for (int u = 0; u < 32 / RPI; u++) {
+          const int r = RPI * u + ln / C::CPR;
+          const s8v v = *(__attribute__((address_space(3))) s8v *)(size_t)(stg + r * D * 2 + ((c ^ (r & (C::CPR - 1))) * 16));
+          if (kbase + r < cur.Skv) *(s8v *)(dst + (int64_t)(cur.sv.k0 + kbase + r) * p.Hkv * D) = v;
+        }
       }
     }
-    return;
-  }
-  short *dst = role == 0 ? p.dv : p.dk;
-#pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int key = kbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-    if (key < Skv) {
-      short *row = dst + ((sv.k0 + key) * p.Hkv + g) * D + lo;
-#pragma unroll
-      for (int dn = 0; dn < C::ND; dn++) row[32 * dn] = TT::cvt_out(acc[dn][r] * sc);
-    }
+    if (MODE == DKDV_ONE) break;
+    T += n;
+    const int ni = MODE == DKDV_SEQ ? nitem : next(item);
+    if (ni >= nitems) break;
+    cur = dkdv_geo<C::BM, BN>(p, ni, rotate);
+    item = ni;
+    if ((MODE != DKDV_SEQ || n == 0) && cur.nsteps > 0) issue(cur, 0, T);  // not prefetched
+    load_kv(cur);
+    wait_vm0();
+    __syncthreads();  // the item's first tile and K/V rows landed
   }
 }
 
-template <class TT, int D, int BN>
-__global__ __launch_bounds__(512, 1) void dense_dkdv_kernel(const Params p) {
+// One workgroup per item (items = the grid), or (SEQ) workgroup b of `grid` takes items in
+// rounds: item b of round 0 and then with the order reversed every other round (keeping each
+// item's XCD, b mod 8, when grid is a multiple of 8), so that the long key blocks at the front of
+// the item order pair with the short ones at its end.
+// D = 64 in the fp16 forms fits 128 VGPRs, i.e. four waves per SIMD: two workgroups per CU (the
+// second bound is waves per SIMD).
+template <class TT, int D, int BN, int MODE>
+__global__ __launch_bounds__(512, (D == 64 && !TT::SPLIT && MODE == DKDV_ONE) ? 4 : 1) void dense_dkdv_kernel(
+    const Params p, int nitems) {
   __shared__ DkdvLds<TT, D, BN> L;
-  dkdv_item<TT, D, BN>(p, blockIdx.x, true, true, L);
+  const int b = blockIdx.x, grid = gridDim.x;
+  int r = 0;
+  auto at = [&](int rr) {
+    const int rev = grid % 8 == 0 ? 8 * (grid / 8 - 1 - b / 8) + b % 8 : grid - 1 - b;
+    return rr * grid + ((rr & 1) ? rev : b);
+  };
+  dkdv_run<TT, D, BN, MODE>(p, b, nitems, [&](int) { return at(++r); }, true, true, L);
 }
 
 // Work-queue form: one workgroup per CU takes items in index order (key blocks longest first)
 // from a counter that starts at zero, so a free CU always gets the next item whatever XCD it is
-// on.  Every workgroup leaves once the counter passes the item count; all its waves see the same
-// item through LDS between two barriers.
+// on.  Thread 0 draws after each item and hands the id over through LDS; every workgroup leaves
+// once the ids pass the item count.
 template <class TT, int D, int BN>
 __global__ __launch_bounds__(512, 1) void dense_dkdv_queue_kernel(const Params p, int nitems) {
   __shared__ DkdvLds<TT, D, BN> L;
-  __shared__ int next;
-  for (;;) {
-    if (threadIdx.x == 0) next = atomicAdd(p.work, 1);
-    __syncthreads();
-    const int u = next;
-    __syncthreads();
-    if (u < 0 || u >= nitems) break;
-    dkdv_item<TT, D, BN>(p, u, false, false, L);
-  }
+  __shared__ int nid;
+  auto next = [&](int) {
+    if (threadIdx.x == 0) nid = atomicAdd(p.work, 1);
+    __syncthreads();  // read before the item's next barrier; rewritten only after it
+    return nid;
+  };
+  const int first = next(0);
+  if (first < nitems) dkdv_run<TT, D, BN, DKDV_QUEUE>(p, first, nitems, next, false, false, L);
 }
 
 template <class TT, int D, int BN>
@@ -413,15 +529,25 @@ static hipError_t launch_dkdv_t(const Params &p, hipStream_t st) {
   const int nkb = ((p.cu ? p.max_seqlen : p.Skv) + DkdvCfg<D, BN>::BM - 1) / DkdvCfg<D, BN>::BM;
   const int64_t items = (int64_t)nkb * (p.cu ? p.nseq : p.B) * p.Hkv * p.hsplit;
   if (items < 1) return hipSuccess;
+  if (items >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
   if (p.work) {
-    int dev = 0, ncu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    int per_cu = 1;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dense_dkdv_queue_kernel<TT, D, BN>, 512, 0);
     if (e != hipSuccess) return e;
-    const int grid = (int)std::min<int64_t>(items, std::max(ncu, 1));
+    const int grid = (int)std::min<int64_t>(items, (int64_t)std::max(ncu, 1) * std::max(per_cu, 1));
     hipLaunchKernelGGL((dense_dkdv_queue_kernel<TT, D, BN>), dim3(grid), dim3(512), 0, st, p, (int)items);
+  } else if constexpr (ATTN_DKDV_SEQ && D == 128) {
+    // D = 128 holds one workgroup per CU: it runs its share of the items back to back.
+    const int grid = (int)std::min<int64_t>(items, std::max(ncu, 1));
+    hipLaunchKernelGGL((dense_dkdv_kernel<TT, D, BN, DKDV_SEQ>), dim3(grid), dim3(512), 0, st, p, (int)items);
   } else {
-    hipLaunchKernelGGL((dense_dkdv_kernel<TT, D, BN>), dim3((unsigned)items), dim3(512), 0, st, p);
+    // D = 64 fits two workgroups per CU, which the hardware fills item by item.
+    hipLaunchKernelGGL((dense_dkdv_kernel<TT, D, BN, DKDV_ONE>), dim3((unsigned)items), dim3(512), 0, st, p,
+                       (int)items);
   }
   return hipGetLastError();
 }

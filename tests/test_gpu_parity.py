@@ -67,6 +67,11 @@ SMALL = [
     small("mha_causal_s1024_h4_bf16", Sq=1024, Skv=1024, Hq=4, Hkv=4, dtype="bf16", seed=108),
     small("gqa_g8_nowindow_ragged_fp16", Sq=333, Skv=333, Hq=8, Hkv=1, seed=109),
     small("gqa_g8_nowindow_ragged_bf16", B=2, Sq=397, Skv=397, Hq=16, Hkv=2, dtype="bf16", seed=110),
+    # More key-block items than CUs: the D = 128 launch runs several items per workgroup, with the
+    # next item's first tile loaded during the current item's last step.
+    small("mha_items_gt_cus_ragged_fp16", B=2, Sq=700, Skv=700, Hq=24, Hkv=24, seed=111),
+    small("gqa_items_gt_cus_ragged_bf16", B=3, Sq=700, Skv=700, Hq=32, Hkv=16, dtype="bf16", seed=112),
+    small("swa_items_gt_cus_fp16", B=3, Sq=800, Skv=800, Hq=16, Hkv=16, window=200, seed=113),
 ] + [small(f"tiny_s{s}", Sq=s, Skv=s, seed=110 + s) for s in (1, 2, 63, 65, 127, 129, 200)]
 
 
