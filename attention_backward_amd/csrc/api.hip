@@ -20,6 +20,22 @@
 #include "attn_bwd.h"
 #include "kernels.h"
 
+namespace attn {
+ArmedEvents &armed_events() {
+  static thread_local ArmedEvents ev;
+  return ev;
+}
+hipError_t settle_events(hipStream_t st) {
+  ArmedEvents &ev = armed_events();
+  const ArmedEvents left = ev;
+  ev = ArmedEvents{};
+  hipError_t e = hipSuccess;
+  if (left.start) e = hipEventRecord(left.start, st);
+  if (e == hipSuccess && left.stop) e = hipEventRecord(left.stop, st);
+  return e;
+}
+}  // namespace attn
+
 #ifndef ATTN_TOPK_MASK_MAX
 #define ATTN_TOPK_MASK_MAX ((int64_t)1 << 30)  // bytes of the top-k key-count mask
 #endif
@@ -174,6 +190,7 @@ int run_fwd(const void *q, const void *k, const void *v, void *o, float *lse, in
   p.nseq = (int)nseq;
   p.max_seqlen = (int)max_seqlen;
   const hipError_t e = attn::launch_dense_fwd(p, (int)D, dtype == ATTN_DT_BF16, (hipStream_t)stream);
+  attn::armed_events() = attn::ArmedEvents{};  // nothing left armed for a later call on this thread
   if (e != hipSuccess) return set_hip_error(e, "kernel launch");
   return ATTN_OK;
 }
@@ -233,8 +250,17 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
   p.nseq = (int)a->nseq;
   p.max_seqlen = (int)a->max_seqlen;
 
+  // Phase events ride on the kernels' own dispatch timestamps (no extra stream packets): the
+  // call's first kernel takes ev[0] as its start, and the kernel ending each phase its stop.
   hipEvent_t *ev = (hipEvent_t *)a->events;
-  hipError_t e = ev ? hipEventRecord(ev[0], st) : hipSuccess;
+  hipError_t e = hipSuccess;
+  auto phase_end = [&](hipEvent_t stop) {  // arm the next kernel's stop, keeping a pending start
+    if (ev) attn::armed_events().stop = stop;
+  };
+  auto settle = [&]() {
+    if (ev && e == hipSuccess) e = attn::settle_events(st);
+  };
+  if (ev) attn::arm_events(ev[0], nullptr);
   if (arith == attn::ARITH_F16B) {
     // Scaled fp16 copies of the inputs; the kernels then read them and the factors in `rescale`.
     unsigned *maxbits = (unsigned *)fx;
@@ -267,8 +293,9 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
   }
   if (!a->topk_idx) {
     // The dQ kernel forms delta and the lse copy in its prologue, so it runs first.
+    phase_end(ev ? ev[1] : nullptr);
     if (e == hipSuccess) e = attn::launch_dense_dq(p, arith, st);
-    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+    settle();
     if (dkdv_queue(a)) {
       char *qb = (char *)ws + 2 * row_stat_bytes(a);
       p.hsplit = dkdv_hsplit(a);
@@ -281,10 +308,16 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
       // Only the counter starts at zero: every slice row inside a sequence is stored by its item.
       if (e == hipSuccess) e = attn::launch_zero((float *)p.work, 64, st);
     }
+    phase_end(ev ? ev[2] : nullptr);
     if (e == hipSuccess) e = attn::launch_dense_dkdv(p, arith, st);
-    if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
-    if (p.hsplit > 1 && e == hipSuccess) e = attn::launch_land_parts(p, arith, st);
-    if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
+    settle();
+    if (p.hsplit > 1) {
+      phase_end(ev ? ev[3] : nullptr);
+      if (e == hipSuccess) e = attn::launch_land_parts(p, arith, st);
+      settle();
+    } else if (e == hipSuccess && ev) {
+      e = hipEventRecord(ev[3], st);  // no landing: the call ends with the dK/dV kernel
+    }
   } else {
     if (e == hipSuccess)
       e = attn::launch_delta(p.o, p.dout, p.ndelta, a->lse, (float *)p.lse, true, a->B, a->Sq, a->Hq, a->Dv,
@@ -300,19 +333,23 @@ int run_bwd(const attn_bwd_args *a, void *ws) {
     if (e == hipSuccess)
       e = attn::launch_topk_count(a->topk_idx, cnt, a->B, a->Sq, a->Skv, a->Hkv, a->topk, (int)skv_pad(a), a->causal,
                                   st);
+    phase_end(ev ? ev[1] : nullptr);
     if (e == hipSuccess) e = attn::launch_sparse_dq(p, arith, st);
-    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+    settle();
+    phase_end(ev ? ev[2] : nullptr);
     if (e == hipSuccess) e = attn::launch_sparse_dkdv(p, cnt, (int)skv_pad(a), dk_acc, dv_acc, arith, st);
-    if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+    settle();
     if (shared) {
+      phase_end(ev ? ev[3] : nullptr);
       if (e == hipSuccess)
         e = attn::launch_land_kv(dk_acc, dv_acc, p.dk, a->B * a->Skv * a->Hkv, a->Dqk, a->Dv, a->scale, p.rescale, bf16,
                                  st);
     } else {
       if (e == hipSuccess) e = attn::launch_land(dk_acc, p.dk, nk, a->scale, p.rescale, 2, bf16, st);
+      phase_end(ev ? ev[3] : nullptr);
       if (e == hipSuccess) e = attn::launch_land(dv_acc, p.dv, nv, 1.0f, p.rescale, 3, bf16, st);
     }
-    if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
+    settle();
   }
   if (e != hipSuccess) return set_hip_error(e, "kernel launch");
   return ATTN_OK;

@@ -539,14 +539,14 @@ static hipError_t launch_dkdv_t(const Params &p, hipStream_t st) {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dense_dkdv_queue_kernel<TT, D, BN>, 512, 0);
     if (e != hipSuccess) return e;
     const int grid = (int)std::min<int64_t>(items, (int64_t)std::max(ncu, 1) * std::max(per_cu, 1));
-    hipLaunchKernelGGL((dense_dkdv_queue_kernel<TT, D, BN>), dim3(grid), dim3(512), 0, st, p, (int)items);
+    launch((dense_dkdv_queue_kernel<TT, D, BN>), dim3(grid), dim3(512), 0, st, p, (int)items);
   } else if constexpr (ATTN_DKDV_SEQ && D == 128) {
     // D = 128 holds one workgroup per CU: it runs its share of the items back to back.
     const int grid = (int)std::min<int64_t>(items, std::max(ncu, 1));
-    hipLaunchKernelGGL((dense_dkdv_kernel<TT, D, BN, DKDV_SEQ>), dim3(grid), dim3(512), 0, st, p, (int)items);
+    launch((dense_dkdv_kernel<TT, D, BN, DKDV_SEQ>), dim3(grid), dim3(512), 0, st, p, (int)items);
   } else {
     // D = 64 fits two workgroups per CU, which the hardware fills item by item.
-    hipLaunchKernelGGL((dense_dkdv_kernel<TT, D, BN, DKDV_ONE>), dim3((unsigned)items), dim3(512), 0, st, p,
+    launch((dense_dkdv_kernel<TT, D, BN, DKDV_ONE>), dim3((unsigned)items), dim3(512), 0, st, p,
                        (int)items);
   }
   return hipGetLastError();
@@ -591,11 +591,11 @@ hipError_t launch_land_parts(const Params &p, int arith, hipStream_t st) {
   if (blocks < 1) return hipSuccess;
   if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   if (arith == ARITH_F16B)
-    hipLaunchKernelGGL(land_parts_kernel<F16B>, dim3((unsigned)blocks), dim3(256), 0, st, p, bps);
+    launch(land_parts_kernel<F16B>, dim3((unsigned)blocks), dim3(256), 0, st, p, bps);
   else if (bf16)
-    hipLaunchKernelGGL(land_parts_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, p, bps);
+    launch(land_parts_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, p, bps);
   else
-    hipLaunchKernelGGL(land_parts_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, p, bps);
+    launch(land_parts_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, p, bps);
   return hipGetLastError();
 }
 

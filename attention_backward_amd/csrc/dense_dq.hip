@@ -306,7 +306,7 @@ static hipError_t launch_dq_t(const Params &p, hipStream_t st) {
   const int nqb = ((p.cu ? p.max_seqlen : p.Sq) + DqCfg<D, BK, SB>::BQ - 1) / DqCfg<D, BK, SB>::BQ;
   const int64_t blocks = (int64_t)nqb * (p.cu ? p.nseq : p.B) * p.Hq;
   if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL((dense_dq_kernel<TT, D, BK, SB>), dim3((unsigned)blocks), dim3(512), 0, st, p);
+  launch((dense_dq_kernel<TT, D, BK, SB>), dim3((unsigned)blocks), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 

@@ -250,7 +250,7 @@ static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t st) {
   const int nqb = ((p.cu ? p.max_seqlen : p.Sq) + FwdCfg<D, BK>::BQ - 1) / FwdCfg<D, BK>::BQ;
   const int64_t blocks = (int64_t)nqb * (p.cu ? p.nseq : p.B) * p.Hq;
   if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL((dense_fwd_kernel<TT, D, BK>), dim3((unsigned)blocks), dim3(512), 0, st, p);
+  launch((dense_fwd_kernel<TT, D, BK>), dim3((unsigned)blocks), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 

@@ -112,13 +112,13 @@ hipError_t launch_f16_prepass(const F16Copy *copies, int ncopies, unsigned *maxb
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
   const dim3 grid((unsigned)blocks, (unsigned)ncopies);
-  hipLaunchKernelGGL(absmax_kernel, grid, dim3(256), 0, st, cs, maxbits);
+  launch(absmax_kernel, grid, dim3(256), 0, st, cs, maxbits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(f16_finalize_kernel, dim3(1), dim3(64), 0, st, maxbits, scales, rescale, c, scale, (int)v_is_k);
+  launch(f16_finalize_kernel, dim3(1), dim3(64), 0, st, maxbits, scales, rescale, c, scale, (int)v_is_k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(to_f16_kernel, grid, dim3(256), 0, st, cs, scales);
+  launch(to_f16_kernel, grid, dim3(256), 0, st, cs, scales);
   return hipGetLastError();
 }
 

@@ -1,11 +1,34 @@
 // kernels.h -- launchers of the attention-backward kernels (host side, C++).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "common.h"
 
 namespace attn {
+
+// Phase timestamps without extra stream packets: arm_events(start, stop) hands the two events to
+// the next kernel that launch() starts on this thread, which takes them as its dispatch
+// timestamps (start when it begins, stop when it ends; either may be null).  settle_events()
+// records, as ordinary stream events, whichever of them no kernel took.
+struct ArmedEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+ArmedEvents &armed_events();  // per host thread
+inline void arm_events(hipEvent_t start, hipEvent_t stop) { armed_events() = ArmedEvents{start, stop}; }
+hipError_t settle_events(hipStream_t st);
+template <class F, class... A>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st, A... args) {
+  ArmedEvents &ev = armed_events();
+  if (ev.start || ev.stop) {
+    const ArmedEvents take = ev;
+    ev = ArmedEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, take.start, take.stop, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  }
+}
 
 // Arithmetic of a call: fp16; bf16 with hi + lo operands for P and dS; or bf16 inputs re-expressed
 // as fp16 copies scaled by powers of two (fp16 products, bf16 outputs, p.rescale set).

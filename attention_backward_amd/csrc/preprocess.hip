@@ -49,7 +49,7 @@ static hipError_t launch_delta_t(const short *o, const short *dout, float *delta
   int64_t blocks = (rows + RPB - 1) / RPB;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL((delta_kernel<TT, DV>), dim3((unsigned)blocks), dim3(256), 0, st, o, dout, delta, lse_in, lse_out,
+  launch((delta_kernel<TT, DV>), dim3((unsigned)blocks), dim3(256), 0, st, o, dout, delta, lse_in, lse_out,
                      negate ? -1.f : 1.f, rows, (int)Sq, (int)Hq);
   return hipGetLastError();
 }

@@ -645,7 +645,7 @@ hipError_t launch_zero(float *buf, int64_t n, hipStream_t st) {
   int64_t blocks = (n4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (float4 *)buf, n4);
+  launch(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (float4 *)buf, n4);
   return hipGetLastError();
 }
 
@@ -659,20 +659,20 @@ hipError_t launch_sparse_dq(const Params &p, int arith, hipStream_t st) {
     const int64_t blocks = (int64_t)p.B * p.Sq * p.Hkv * (p.G / 64);
     if (blocks < 1) return hipSuccess;
     if (arith == ARITH_F16B)
-      hipLaunchKernelGGL((sparse_dq64_kernel<F16B, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+      launch((sparse_dq64_kernel<F16B, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
     else
-      hipLaunchKernelGGL((sparse_dq64_kernel<F16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+      launch((sparse_dq64_kernel<F16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
     return hipGetLastError();
   }
   const int nhb = (p.G + SpCfg<576, 512>::HB - 1) / SpCfg<576, 512>::HB;
   const int64_t blocks = (int64_t)p.B * p.Sq * p.Hkv * nhb;
   if (blocks < 1) return hipSuccess;
   if (arith == ARITH_BF16)
-    hipLaunchKernelGGL((sparse_dq_kernel<BF16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+    launch((sparse_dq_kernel<BF16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   else if (arith == ARITH_F16B)
-    hipLaunchKernelGGL((sparse_dq_kernel<F16B, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+    launch((sparse_dq_kernel<F16B, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((sparse_dq_kernel<F16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+    launch((sparse_dq_kernel<F16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -683,9 +683,9 @@ hipError_t launch_land(const float *acc, short *out, int64_t n, float scale, con
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(land_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, acc, out, n8, scale, rescale, which);
+    launch(land_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, acc, out, n8, scale, rescale, which);
   else
-    hipLaunchKernelGGL(land_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, acc, out, n8, scale, rescale, which);
+    launch(land_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, acc, out, n8, scale, rescale, which);
   return hipGetLastError();
 }
 
@@ -697,10 +697,10 @@ hipError_t launch_land_kv(const float *dk_acc, const float *dv_acc, short *out, 
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(land_kv_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, dk_acc, dv_acc, out, n8,
+    launch(land_kv_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, dk_acc, dv_acc, out, n8,
                        (int)(Dqk / 8), (int)(Dv / 8), scale, rescale);
   else
-    hipLaunchKernelGGL(land_kv_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, dk_acc, dv_acc, out, n8,
+    launch(land_kv_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, dk_acc, dv_acc, out, n8,
                        (int)(Dqk / 8), (int)(Dv / 8), scale, rescale);
   return hipGetLastError();
 }

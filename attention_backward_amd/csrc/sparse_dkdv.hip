@@ -378,7 +378,7 @@ hipError_t launch_topk_count(const int32_t *idx, uint16_t *cnt, int64_t B, int64
   if (topk_count_by_rows(skv_pad)) {
     const int64_t rows = B * Sq * Hkv;
     if (rows < 1) return hipSuccess;
-    hipLaunchKernelGGL(topk_count_rows_kernel, dim3((unsigned)rows), dim3(256), (size_t)skv_pad * 2, st, idx,
+    launch(topk_count_rows_kernel, dim3((unsigned)rows), dim3(256), (size_t)skv_pad * 2, st, idx,
                        (uint32_t *)cnt, (int)topk, (int)Sq, (int)Skv, (int)Hkv, skv_pad, causal);
     return hipGetLastError();
   }
@@ -386,7 +386,7 @@ hipError_t launch_topk_count(const int32_t *idx, uint16_t *cnt, int64_t B, int64
   int64_t blocks = (n + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL(topk_count_kernel, dim3((unsigned)blocks), dim3(256), 0, st, idx, (uint32_t *)cnt, n, (int)topk,
+  launch(topk_count_kernel, dim3((unsigned)blocks), dim3(256), 0, st, idx, (uint32_t *)cnt, n, (int)topk,
                      (int)Sq, (int)Skv, (int)Hkv, skv_pad, causal);
   return hipGetLastError();
 }
@@ -404,13 +404,13 @@ hipError_t launch_sparse_dkdv(const Params &p, const uint16_t *cnt, int skv_pad,
   const int64_t blocks = (int64_t)nchunk * nkb * p.B * p.Hkv;
   if (blocks < 1) return hipSuccess;
   if (arith == ARITH_BF16)
-    hipLaunchKernelGGL((sparse_dkdv_kernel<BF16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p, cnt, skv_pad,
+    launch((sparse_dkdv_kernel<BF16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p, cnt, skv_pad,
                        qchunk, nchunk, dk_acc, dv_acc);
   else if (arith == ARITH_F16B)  // rescaled inputs: dS is brought back to its own scale
-    hipLaunchKernelGGL((sparse_dkdv_kernel<F16B, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p, cnt, skv_pad,
+    launch((sparse_dkdv_kernel<F16B, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p, cnt, skv_pad,
                        qchunk, nchunk, dk_acc, dv_acc);
   else
-    hipLaunchKernelGGL((sparse_dkdv_kernel<F16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p, cnt, skv_pad,
+    launch((sparse_dkdv_kernel<F16, 576, 512>), dim3((unsigned)blocks), dim3(256), 0, st, p, cnt, skv_pad,
                        qchunk, nchunk, dk_acc, dv_acc);
   return hipGetLastError();
 }

@@ -34,6 +34,19 @@ LOG2E = 1.4426950408889634
 METRIC = "attn-bwd TFLOP/s (causal-adjusted) + % of MI355X fp16/bf16 MFMA peak"
 
 
+def carries_events(args, s: int) -> bool:
+    """Whether timed step s records the per-kernel events.  Each event costs the stream a few
+    microseconds (a timestamp packet, or a dispatch with timestamps), so only every N-th timed step
+    carries them: the kernel durations are still taken inside the timed region, on its stream,
+    while the step time carries 1/N of that cost."""
+    n = max(1, args.events_every)
+    return s % n == n - 1 or (args.steps < n and s == args.steps - 1)
+
+
+def timed_steps(args) -> list:
+    return [s for s in range(args.steps) if carries_events(args, s)]
+
+
 # HBM traffic of the dominant kernel per launch, from two rocprofv3 counter runs (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch), each scaled by what the counter reads for an fp16->f32 copy of
 # known size (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000).  Keyed by the hash of the kernel's source
@@ -273,15 +286,20 @@ def bench_forward(args, w, ab, with_bwd=False):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in timed_steps(args)]
     t0 = time.perf_counter()
-    for row in ev:
-        row[0].record(stream)
+    it = iter(ev)
+    for s in range(args.steps):
+        row = next(it) if carries_events(args, s) else None
+        if row:
+            row[0].record(stream)
         ab.attn_fwd(q, k, v, o, lse, w.scale, causal=w.causal, window=w.window, stream=stream)
-        row[1].record(stream)
+        if row:
+            row[1].record(stream)
         if with_bwd:
             ab.attn_bwd_ex(a)
-        row[2].record(stream)
+        if row:
+            row[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [row[0].elapsed_time(row[1]) * 1e3 for row in ev]
@@ -361,21 +379,27 @@ def bench_varlen(args, vw, ab):
     torch.cuda.synchronize()
     import ctypes
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in timed_steps(args)]
     for row in ev:
         for e in row:
             e.record(stream)
     torch.cuda.synchronize()
     ev_arrays = [(ctypes.c_void_p * 4)(*[e.cuda_event for e in row]) for row in ev]
     t0 = time.perf_counter()
+    j_ = 0
     for s_ in range(args.steps):
-        if args.forward:
-            ev[s_][0].record(stream)
+        if not carries_events(args, s_):
+            a.events = None
             call()
-            ev[s_][1].record(stream)
+        elif args.forward:
+            ev[j_][0].record(stream)
+            call()
+            ev[j_][1].record(stream)
+            j_ += 1
         else:
-            a.events = ctypes.cast(ev_arrays[s_], ctypes.c_void_p)
+            a.events = ctypes.cast(ev_arrays[j_], ctypes.c_void_p)
             call()
+            j_ += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     a.events = None
@@ -432,6 +456,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--events-every", type=int, default=4,
+                    help="timed steps that carry the per-kernel events: every N-th (1 = all); the\n"
+                         "events' stream work is then a 1/N share of the measured step time")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=synth.HEADLINE,
                     choices=sorted(synth.WORKLOADS) + sorted(synth.VARLEN_WORKLOADS))
@@ -491,9 +518,9 @@ def main():
         ab.attn_bwd_ex(a)
     torch.cuda.synchronize()
 
-    # Timed region: exactly K back-to-back steps, with 4 events per step recorded by the library
-    # on its launch stream around its three kernels.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Timed region: exactly K back-to-back steps; every --events-every-th one passes 4 events that
+    # the library records on its launch stream at its phase boundaries (dispatch timestamps).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in timed_steps(args)]
     import ctypes
 
     for row in ev:
@@ -503,8 +530,13 @@ def main():
     ev_arrays = [(ctypes.c_void_p * 4)(*[e.cuda_event for e in row]) for row in ev]
     assert all(h for arr in ev_arrays for h in arr), "HIP event handles must be non-null"
     t0 = time.perf_counter()
+    j = 0
     for s in range(args.steps):
-        a.events = ctypes.cast(ev_arrays[s], ctypes.c_void_p)
+        if carries_events(args, s):
+            a.events = ctypes.cast(ev_arrays[j], ctypes.c_void_p)
+            j += 1
+        else:
+            a.events = None
         ab.attn_bwd_ex(a)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -594,6 +626,7 @@ def main():
                      "algorithmic_flops_per_launch": main_flops},
         "kernels_us_median": {kname: round(v_, 2) for kname, v_ in med.items()},
         "kernels": kernels,
+        "kernel_events": {"every_nth_timed_step": max(1, args.events_every), "samples": len(ev)},
         "cold_call_us": None if not cold else {
             "median": round(statistics.median(cold), 2), "mean": round(statistics.fmean(cold), 2),
             "std": round(statistics.pstdev(cold), 2), "min": round(min(cold), 2),

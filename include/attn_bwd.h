@@ -85,14 +85,19 @@ typedef struct {
   size_t workspace_bytes;
   void *stream;                     /* hipStream_t                                             */
   void *events;                     /* optional, NULL or an array of 4 hipEvent_t created by the
-                                       caller, recorded on `stream` between the phases: dense =
-                                       before the dQ kernel (which also forms delta and the lse
-                                       copy) | after it | after the dK/dV kernel | after the
-                                       landing pass of a split packed call (else again after
-                                       the dK/dV kernel); top-k = before the preprocess | after
-                                       it, the zero-fill, the key counts and the dQ kernel |
-                                       after the dK/dV kernel | after the landing passes
-                                       (per-phase timing without changing the work)          */
+                                       caller, marking on `stream` the phase boundaries: dense =
+                                       the start of the call's first kernel (the dQ kernel,
+                                       which also forms delta and the lse copy, or the bf16
+                                       pre-pass) | the end of the dQ kernel | the end of the
+                                       dK/dV kernel | the end of the landing pass of a split
+                                       packed call (else recorded right after the dK/dV
+                                       kernel); top-k = the start of the preprocess | the end
+                                       of the dQ kernel (after the zero-fill and the key
+                                       counts) | the end of the dK/dV kernel | the end of the
+                                       landing passes.  Events at kernel ends and starts are
+                                       taken as those kernels' dispatch timestamps
+                                       (hipExtLaunchKernel), with no extra stream packets; the
+                                       work is unchanged                                        */
   int32_t kv_shared;                /* 0, or 1 for the shared-latent form of the top-k path (the
                                        TileLang PR #2592 page's sparse MLA op, which returns dq and
                                        dkv): k holds [B,Skv,Hkv,Dqk] rows whose first Dv columns are
