@@ -294,6 +294,7 @@ __device__ __forceinline__ void dkdv_run(const Params &p, int item, const int ni
   const Factors fac = factors(p);
 
   DkdvItem cur = dkdv_geo<C::BM, BN>(p, item, rotate);
+  if (MODE == DKDV_ONE && !cur.live) return;  // a packed sequence shorter than the longest
   load_kv(cur);
   int T = 0;  // steps run so far: buffer parity across items
   if (cur.nsteps > 0) issue(cur, 0, 0);
@@ -304,6 +305,7 @@ __device__ __forceinline__ void dkdv_run(const Params &p, int item, const int ni
     const int nitem = MODE == DKDV_SEQ ? next(item) : nitems;
     const bool has_next = nitem < nitems;  // known in advance (DKDV_SEQ only)
     const int n = cur.nsteps;
+    const int T0 = MODE == DKDV_ONE ? 0 : T;  // running step count at the item's first step
     const int kbase = cur.k0 + 32 * kgrp;
     // The range [qlo, qhi] of query rows allowed to see the lane's key.
     const int kj = kbase + lo;
@@ -317,18 +319,19 @@ __device__ __forceinline__ void dkdv_run(const Params &p, int item, const int ni
              (cur.k0 + C::BM <= cur.Skv);
     };
     // The loads of step t + 1: the item's own next step, or at its last step the next item's
-    // first.  A step ends by waiting for them, except the last, which leaves the next item's
-    // tile in flight.
+    // first.  A step ends by waiting for them; in the fixed item sequence the last step leaves the
+    // next item's tile in flight (16K GQA: 6% faster), while the one-item launch waits at every
+    // step (the conditional wait cost its D = 64 steps 8%).
     auto issue_next = [&](int t) {
       if (t + 1 < n) {
-        issue(cur, t + 1, T + t + 1);
+        issue(cur, t + 1, T0 + t + 1);
       } else if (has_next) {
         const DkdvItem nx = dkdv_geo<C::BM, BN>(p, nitem, rotate);
-        if (nx.nsteps > 0) issue(nx, 0, T + t + 1);
+        if (nx.nsteps > 0) issue(nx, 0, T0 + t + 1);
       }
     };
     auto end_step = [&](int t) {
-      if (t + 1 < n) wait_vm0();
+      if (MODE != DKDV_SEQ || t + 1 < n) wait_vm0();
       __syncthreads();
     };
 #pragma unroll
@@ -336,12 +339,12 @@ __device__ __forceinline__ void dkdv_run(const Params &p, int item, const int ni
 
     if (role == 0) {
       for (int t = 0; t < n; t++) {
-        const int buf = (T + t) & 1;
+        const int buf = (T0 + t) & 1;
         const int q0 = step_q0(cur, t);
         issue_next(t);
         f16v s[C::MB] = {};
         mfma_prio_hi();
-        phase1(s, q_s[(T + t) % 3]);
+        phase1(s, q_s[(T0 + t) % 3]);
         mfma_prio_lo();
         s8v pa[C::KS], pl[C::KS];
         auto softmax = [&](auto masked) {
@@ -380,9 +383,9 @@ __device__ __forceinline__ void dkdv_run(const Params &p, int item, const int ni
     } else {
       s8v da[C::KS], dl[C::KS];  // dS of the previous step (B operands)
       for (int t = 0; t < n; t++) {
-        const int buf = (T + t) & 1;
+        const int buf = (T0 + t) & 1;
         issue_next(t);
-        if (t > 0) phase2(da, dl, q_s[(T + t + 2) % 3]);  // dK^T += Q^T dS of step t-1
+        if (t > 0) phase2(da, dl, q_s[(T0 + t + 2) % 3]);  // dK^T += Q^T dS of step t-1
         // dP accumulators start from minus delta of their query rows (register 4 j + i of block
         // mb is row 32 mb + 8 j + 4 hi + i), so the products leave dP - delta in them.
         f16v s[C::MB];
@@ -415,7 +418,7 @@ __device__ __forceinline__ void dkdv_run(const Params &p, int item, const int ni
           }
         end_step(t);  // next tile landed; P consumed
       }
-      if (n > 0) phase2(da, dl, q_s[(T + n - 1) % 3]);
+      if (n > 0) phase2(da, dl, q_s[(T0 + n - 1) % 3]);
     }
 
     // Epilogue: dV (P role) or scale * dK (dS role), cast once, BSHD at the KV head.  The
@@ -433,7 +436,7 @@ __device__ __forceinline__ void dkdv_run(const Params &p, int item, const int ni
           for (int j = 0; j < 4; j++)
             *(f4v *)(row + 32 * dn + 8 * j) = f4v{acc[dn][4 * j], acc[dn][4 * j + 1], acc[dn][4 * j + 2], acc[dn][4 * j + 3]};
       }
-    } else {
+    } else if (cur.live) {
       // The wave's 32 x D block goes through LDS so that the global stores are whole rows (16
       // lanes x 16 bytes per 256-byte row): staged row-major, 16-byte chunk c of row r at chunk
       // c ^ (r mod CPR).  Staging space, 32 D 2 bytes per wave, two waves per buffer: the two Q
@@ -444,9 +447,9 @@ __device__ __forceinline__ void dkdv_run(const Params &p, int item, const int ni
       static_assert(2 * WB <= (int)sizeof(q_s[0]) && 2 * WB <= (int)sizeof(p_s) + (int)sizeof(ph_s),
                     "staging space");
       const int rg = w >> 1;
-      const uint32_t stg = (rg == 0   ? lds_addr(&q_s[(T + n + 2) % 3][0])
-                            : rg == 1 ? lds_addr(&q_s[(T + n + 1) % 3][0])
-                            : rg == 2 ? lds_addr(&do_s[(T + n + 1) & 1][0])
+      const uint32_t stg = (rg == 0   ? lds_addr(&q_s[(T0 + n + 2) % 3][0])
+                            : rg == 1 ? lds_addr(&q_s[(T0 + n + 1) % 3][0])
+                            : rg == 2 ? lds_addr(&do_s[(T0 + n + 1) & 1][0])
                                       : (PH ? lds_addr(&ph_s[0][0][0]) : lds_addr(&p_s[0][0][0][0]))) +
                            (w & 1) * WB;
       // Lane terms recomputed here (opaque) rather than hoisted out of the item loop, where they
@@ -463,7 +466,7 @@ __device__ __forceinline__ void dkdv_run(const Params &p, int item, const int ni
           const int c = 4 * dn + j;
           *(__attribute__((address_space(3))) s4v *)(size_t)(wr + ((c ^ swl) * 16)) = o;
         }
-      if (cur.live) {
+      {
         constexpr int RPI = 64 / C::CPR;  // rows per store instruction
         const int c = ln % C::CPR;
         short *dst = (role == 0 ? p.dv : p.dk) + (int64_t)cur.g * D + 8 * c;
