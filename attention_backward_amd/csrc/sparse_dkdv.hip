@@ -13,15 +13,18 @@
 // atomics.  A key block's query range is cut into chunks so that the grid balances; each chunk
 // adds its finished 32-key dK/dV block once into f32 accumulators that a landing pass casts.
 //
-// Workgroup: 4 wave64s (one per SIMD, up to 512 VGPRs each), 32 keys of one (batch, KV head),
-// one query chunk.  A step is one query i and a block of 32 of its KV head's query heads.  Wave w
-// owns the 16-key x 16-head block (w&1, w>>1) of S^T = K Q^T and dP^T = V dO^T (v_mfma 16x16x32,
-// the block's K and V rows resident in registers), forms P^T = cnt * exp2(S^T c - lse) and
-// dS^T = P^T (dP^T - delta) for it, and accumulates a 128-wide slice of dV += P^T dO and a slice
-// of dK += dS^T Q (5, 5, 4, 4 blocks of 32), reading the whole step's P^T / dS^T from LDS.
-// Q and dO rows of the step (32 heads) are double-buffered in LDS, loaded directly from global
-// memory; P^T and dS^T cross as 16-bit [key][head] tiles (hi and, for bf16, lo halves).  Every
-// LDS operand is read a few products ahead through a register ring.
+// Workgroup: 4 wave64s (one per SIMD, up to 512 registers each), 32 keys of one (batch, KV head),
+// one query chunk.  A step is one query i and a block of 16 of its KV head's query heads.  The
+// waves split by role and run one step apart:
+//   - waves 0 and 1 (scoring) hold the K and V rows of keys 16w..16w+15 as the A operands of
+//     S^T = K Q^T and dP^T = V dO^T (v_mfma 16x16x32), form P^T = cnt * exp2(S^T c - lse) and
+//     dS^T = P^T (dP^T - delta) of step t and stage them in LDS as 16-bit [key][head] blocks
+//     (hi and, for bf16, lo halves);
+//   - waves 2 and 3 (accumulating) add step t-1 into dV += P^T dO and dK += dS^T Q (32x32x16
+//     products, 8 dV and 7 dK blocks of 32 columns each; the scoring waves take the last 4 dK
+//     blocks, 2 each), and load the Q / dO tiles of step t+1 through registers.
+// Tiles go round three LDS buffers (t+1 stored, t scored, t-1 accumulated) and one barrier per
+// step hands them on.  Every LDS operand is read a few products ahead through a register ring.
 #include "common.h"
 #include "kernels.h"
 
@@ -73,23 +76,26 @@ __global__ __launch_bounds__(256) void topk_count_rows_kernel(const int32_t *__r
 
 template <int DQK, int DV>
 struct SkCfg {
-  static constexpr int BM = 32;           // keys per workgroup
-  static constexpr int HB = 32;           // query heads per step
-  static constexpr int CQ = DQK / 8;      // 16-byte chunks per Q row
-  static constexpr int CV = DV / 8;       // 16-byte chunks per dO row
-  static constexpr int KQ = DQK / 32;     // 16x16x32 k-steps over Dqk
-  static constexpr int KV = DV / 32;      // 16x16x32 k-steps over Dv
-  static constexpr int NQ = DQK / 32;     // 32-wide blocks of dK
-  static constexpr int NVW = DV / 128;    // 32-wide blocks of dV per wave (4 waves)
-  static constexpr int LQ = HB * CQ / 256;  // 16-byte loads per thread: Q tile
-  static constexpr int LD = HB * CV / 256;  // dO tile
-  static_assert(DV % 128 == 0 && DQK % 32 == 0, "head dims");
-  static_assert((HB * CQ) % 256 == 0 && (HB * CV) % 256 == 0, "tiles split into whole workgroup loads");
+  static constexpr int BM = 32;              // keys per workgroup
+  static constexpr int HB = 16;              // query heads per step
+  static constexpr int CQ = DQK / 8;         // 16-byte chunks per Q row
+  static constexpr int CV = DV / 8;          // 16-byte chunks per dO row
+  static constexpr int KQ = DQK / 32;        // 16x16x32 k-steps over Dqk
+  static constexpr int KV = DV / 32;         // 16x16x32 k-steps over Dv
+  static constexpr int NQ = DQK / 32;        // 32-wide blocks of dK
+  static constexpr int NV = DV / 32;         // 32-wide blocks of dV
+  static constexpr int NVW = NV / 2;         // dV blocks of each accumulating wave
+  static constexpr int NKS = 2;              // dK blocks of each scoring wave (the last 2 NKS)
+  static constexpr int NKK = (NQ - 2 * NKS) / 2;  // dK blocks of each accumulating wave
+  static constexpr int LQ = HB * CQ / 128;   // 16-byte loads per lane of the two loading waves: Q tile
+  static constexpr int LD = HB * CV / 128;   // dO tile
+  static constexpr int NLD = LQ + LD;
+  static_assert(NV % 2 == 0 && DQK % 32 == 0 && NQ > 2 * NKS && (NQ - 2 * NKS) % 2 == 0, "head dims");
+  // An accumulating wave holds NVW + NKK 32x32 f32 blocks in its 256 AGPRs; at 16 blocks the
+  // compiler starts copying accumulators through VGPRs inside the loop.
+  static_assert(NVW + NKK <= 15, "accumulators of one wave");
+  static_assert((HB * CQ) % 128 == 0 && (HB * CV) % 128 == 0, "tiles split into whole loads of two waves");
 };
-
-// dK blocks of wave v: [first, first + count) out of NQ (NQ = 18: 5, 5, 4, 4).
-__host__ __device__ constexpr int dk_first(int v, int nq) { return v * (nq / 4) + (v < nq % 4 ? v : nq % 4); }
-__host__ __device__ constexpr int dk_count(int v, int nq) { return nq / 4 + (v < nq % 4 ? 1 : 0); }
 
 // 16x16x32 products (lane layouts measured on MI355X with an in-bounds probe):
 //   A lane l: A[m = l%16][k = 8*(l/16) + e];  B lane l: B[k = 8*(l/16) + e][n = l%16];
@@ -128,12 +134,14 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
   using C = SkCfg<DQK, DV>;
   constexpr int PF = 3;
   constexpr bool SPLIT = TT::SPLIT && ATTN_SPARSE_DKDV_SPLIT;
-  __shared__ __attribute__((aligned(16))) short q_s[2][C::HB * DQK];
-  __shared__ __attribute__((aligned(16))) short do_s[2][C::HB * DV];
-  __shared__ __attribute__((aligned(16))) short st_p[2][C::BM * C::HB];  // P^T [key][head], hi / lo
-  __shared__ __attribute__((aligned(16))) short st_ds[2][C::BM * C::HB];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][C::HB], dl_s[2][C::HB];
-  __shared__ __attribute__((aligned(16))) uint16_t cnt_s[2][C::BM];
+  constexpr int NH = SPLIT ? 2 : 1;                   // staged halves of P^T and dS^T
+  constexpr int TQ = C::HB * DQK, TD = C::HB * DV;    // elements per Q / dO tile
+  __shared__ __attribute__((aligned(16))) short q_s[3][TQ];
+  __shared__ __attribute__((aligned(16))) short do_s[3][TD];
+  __shared__ __attribute__((aligned(16))) short st_p[2][NH][C::BM * C::HB];  // P^T [key][head], hi / lo
+  __shared__ __attribute__((aligned(16))) short st_ds[2][NH][C::BM * C::HB];
+  __shared__ __attribute__((aligned(16))) float lse_s[3][C::HB], dl_s[3][C::HB];
+  __shared__ __attribute__((aligned(16))) uint16_t cnt_s[3][C::BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,217 +166,270 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
   if (qc >= nchunk || i_end <= i_beg) return;  // uniform: the whole workgroup leaves
   const int nsteps = (i_end - i_beg) * nhb;
 
-  // Resident A operands A[m = key][k = d] of this wave's 16 keys (16x16x32 layout): K and V rows.
-  // Key rows past Skv are clamped (their counts are 0).
-  const int kh = w & 1, hh = w >> 1;
-  s8v kr[C::KQ], vr[C::KV];
-  {
-    const int key = min(j0 + 16 * kh + i16, p.Skv - 1);
-    const int64_t r = ((int64_t)b * p.Skv + key) * p.Hkv + g;
-#pragma unroll
-    for (int kk = 0; kk < C::KQ; kk++) kr[kk] = *(const s8v *)(p.k + r * DQK + 32 * kk + 8 * g16);
-#pragma unroll
-    for (int kk = 0; kk < C::KV; kk++) vr[kk] = *(const s8v *)(p.v + r * p.v_ld + 32 * kk + 8 * g16);
-  }
-
-  // Accumulators (32 keys x 32-wide d blocks): dV blocks [4w, 4w+4), dK blocks [kf, kf + kn).
-  constexpr int NKW = (C::NQ + 3) / 4;
-  f16v av[C::NVW], ak[NKW];
-#pragma unroll
-  for (int u = 0; u < C::NVW; u++) av[u] = f16v{};
-#pragma unroll
-  for (int u = 0; u < NKW; u++) ak[u] = f16v{};
-  const int kf = dk_first(w, C::NQ), kn = dk_count(w, C::NQ);
-
-  // Step t -> query i = i_beg + t / nhb, head block t % nhb.  Loads of a step: Q and dO rows of
-  // its heads (rows past the group's end repeat its last head; masked below), lse and delta,
-  // and the count row of the 32 keys.  Tile slot s = 256 u + tid is physical chunk s % C of
-  // row s / C and holds logical chunk (s % C) ^ sw(row); the lanes' byte offsets for a full head
-  // block are computed once, and a ragged last block clamps its rows per step.
-  uint32_t qoff[C::LQ], doff[C::LD];
-#pragma unroll
-  for (int u = 0; u < C::LQ; u++) {
-    const int s = 256 * u + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sk_sw<DQK>(r);
-    qoff[u] = (uint32_t)(r * DQK + 8 * ch) * 2;
-  }
-#pragma unroll
-  for (int u = 0; u < C::LD; u++) {
-    const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sk_sw<DV>(r);
-    doff[u] = (uint32_t)(r * DV + 8 * ch) * 2;
-  }
-  const uint32_t q_lds = lds_addr(&q_s[0][0]), do_lds = lds_addr(&do_s[0][0]);
-  auto issue = [&](int t, int buf) {
-    const int i = i_beg + t / nhb, hb0 = (t % nhb) * C::HB;
-    const int nh = min(C::HB, p.G - hb0);
-    const int64_t qrow = ((int64_t)b * p.Sq + i) * p.Hq + g * p.G + hb0;
-    const int64_t nrows = (int64_t)p.B * p.Sq * p.Hq;
-    const i4v rq = buf_rsrc(p.q + qrow * DQK, (uint64_t)(nrows - qrow) * DQK * 2);
-    const i4v rd = buf_rsrc(p.dout + qrow * DV, (uint64_t)(nrows - qrow) * DV * 2);
-    const uint32_t qb = q_lds + buf * (C::HB * DQK * 2) + 1024 * w, db = do_lds + buf * (C::HB * DV * 2) + 1024 * w;
-    if (nh == C::HB) {
-#pragma unroll
-      for (int u = 0; u < C::LQ; u++) b2lds16_at(rq, qoff[u], qb + 4096 * u);
-#pragma unroll
-      for (int u = 0; u < C::LD; u++) b2lds16_at(rd, doff[u], db + 4096 * u);
-    } else {
-#pragma unroll
-      for (int u = 0; u < C::LQ; u++) {
-        const int s = 256 * u + tid, r = s / C::CQ, ch = (s % C::CQ) ^ sk_sw<DQK>(r);
-        b2lds16_at(rq, (uint32_t)(min(r, nh - 1) * DQK + 8 * ch) * 2, qb + 4096 * u);
-      }
-#pragma unroll
-      for (int u = 0; u < C::LD; u++) {
-        const int s = 256 * u + tid, r = s / C::CV, ch = (s % C::CV) ^ sk_sw<DV>(r);
-        b2lds16_at(rd, (uint32_t)(min(r, nh - 1) * DV + 8 * ch) * 2, db + 4096 * u);
-      }
-    }
-    // One wave per small row (the LDS base of a direct load is per wave): lane l writes word l.
-    if (w >= 2) {
-      const int64_t l0 = ((int64_t)b * p.Hq + g * p.G + hb0) * p.Sq + i;
-      const int64_t nl = (int64_t)p.B * p.Hq * p.Sq;
-      const i4v rl = buf_rsrc((w == 3 ? (const float *)p.lse : (const float *)p.ndelta) + l0, (uint64_t)(nl - l0) * 4);
-      if (lane < C::HB) b2lds4(rl, (uint32_t)(min(lane, nh - 1) * p.Sq) * 4, w == 3 ? &lse_s[buf][0] : &dl_s[buf][0]);
-    } else if (w == 1) {
-      const int64_t e0 = (((int64_t)b * p.Hkv + g) * p.Sq + i) * skv_pad + j0;
-      const int64_t ne = (int64_t)p.B * p.Hkv * p.Sq * skv_pad;
-      const i4v rc = buf_rsrc(cnt + e0, (uint64_t)(ne - e0) * 2);
-      if (lane < C::BM / 2) b2lds4(rc, (uint32_t)(4 * lane), &cnt_s[buf][0]);
-    }
-  };
-
-  // Transposed read of B[k = head][n = d] from a [head][d] tile (16 heads 16*ks + 8*hi + e).
-  auto trB = [&](const short *tile, bool is_q, int ks, int nb) {
+  // Step t is query i_beg + t / nhb and the head block t % nhb of its KV head's group.  Waves 0
+  // and 1 form S^T, dP^T, P^T and dS^T of step t for keys 16w..16w+15 and stage P^T / dS^T; waves
+  // 2 and 3 meanwhile add step t-1 into dV and dK and load the tiles of step t+1.  The tiles go
+  // round three buffers (t+1 loading, t scored, t-1 accumulated), the staging round two, and
+  // one barrier per step hands both on.  The loop runs one extra step to accumulate the last.
+  // Transposed read of B[k = head][n = d] from a [head][d] tile (heads 8*hi + e).
+  auto trB = [&](const short *tile, bool is_q, int nb) {
     const int rowlen = is_q ? DQK : DV;
     const int col = 32 * nb + 16 * (g16 & 1) + 4 * (i16 & 3);
     s4v part[2];
 #pragma unroll
     for (int half = 0; half < 2; half++) {
-      const int row = 16 * ks + 8 * hi + 4 * half + (i16 >> 2);
+      const int row = 8 * hi + 4 * half + (i16 >> 2);
       const int ch = (col >> 3) ^ (is_q ? sk_sw<DQK>(row) : sk_sw<DV>(row));
       part[half] = lds_tr4(&tile[row * rowlen + 8 * ch + (col & 7)]);
     }
     return cat8(part[0], part[1]);
   };
-
-  if (nsteps > 0) issue(0, 0);
-  wait_vm0();
-  __syncthreads();
-
-  const int head = 16 * hh + i16;  // this lane's head column in the S^T / dP^T block
-  const int swq = sk_sw<DQK>(head), swv = sk_sw<DV>(head);
-  for (int t = 0; t < nsteps; t++) {
-    const int buf = t & 1;
-    const int nh = min(C::HB, p.G - (t % nhb) * C::HB);
-    if (t + 1 < nsteps) issue(t + 1, buf ^ 1);
-
-    // S^T and dP^T of the wave's block: B = Q / dO rows B[k = d][n = head] (natural reads of
-    // the head's row).  The S and dP products alternate, so consecutive MFMAs never wait on
-    // each other's accumulator; one ring carries the reads of both.
-    f4v sv = f4v{}, dpv = f4v{};
-    {
-      const short *qrow = &q_s[buf][head * DQK];
-      const short *drow = &do_s[buf][head * DV];
-      // order: S0 P0 S1 P1 ... S(KV-1) P(KV-1) S(KV) ... S(KQ-1)
-      auto is_s = [](int n) { return n >= 2 * C::KV || (n & 1) == 0; };
-      auto kidx = [](int n) { return n >= 2 * C::KV ? n - C::KV : n >> 1; };
-      ring_pipeline<C::KQ + C::KV, PF>(
-          [&](int n) {
-            const int kk = kidx(n);
-            return is_s(n) ? *(const s8v *)&qrow[8 * ((4 * kk + g16) ^ swq)]
-                           : *(const s8v *)&drow[8 * ((4 * kk + g16) ^ swv)];
-          },
-          [&](int n, s8v bv) {
-            if (is_s(n))
-              sv = mfma16<TT>(kr[kidx(n)], bv, sv);
-            else
-              dpv = mfma16<TT>(vr[kidx(n)], bv, dpv);
-          });
-    }
-    // P^T and dS^T of the block: register r is key 16*kh + 4*g16 + r, head 16*hh + i16.
-    {
-      const float l = lse_s[buf][head], dl = dl_s[buf][head];
-      const bool hok = head < nh;
+  // Add finished 32-key blocks (unscaled) into the f32 accumulators at Hkv: register r of a
+  // block is key j0 + 8*(r/4) + 4*hi + r%4, column 32*(first + u) + lo.
+  // The block count is a template argument: indexing the accumulator array with a run-time
+  // count would move the whole array to scratch memory.
+  auto add_blocks = [&](auto nblk, const f16v *acc, float *dst, int rowlen, int first) {
+    constexpr int N = decltype(nblk)::value;
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int key = 16 * kh + 4 * g16 + r;
-        const float c = (float)cnt_s[buf][key];
-        const float pr = (hok && c > 0.f) ? c * exp2f_hw(sv[r] * fac.c - l) : 0.f;
-        const float ds = ds_of<TT>(pr, dpv[r] + dl, fac);  // dl = minus delta
-        const short ph = TT::cvt(pr), dh = TT::cvt(ds);
-        st_p[0][key * C::HB + head] = ph;
-        st_ds[0][key * C::HB + head] = dh;
+    for (int r = 0; r < 16; r++) {
+      const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (key < p.Skv) {
+        const int64_t row = ((int64_t)b * p.Skv + key) * p.Hkv + g;
+#pragma unroll
+        for (int u = 0; u < N; u++) unsafeAtomicAdd(&dst[row * rowlen + 32 * (first + u) + lo], acc[u][r]);
+      }
+    }
+  };
+
+  if (w < 2) {
+    // Resident A operands A[m = key][k = d] of this wave's 16 keys (16x16x32 layout): K and V
+    // rows.  Key rows past Skv are clamped (their counts are 0).
+    s8v kr[C::KQ], vr[C::KV];
+    {
+      const int key = min(j0 + 16 * w + i16, p.Skv - 1);
+      const int64_t r = ((int64_t)b * p.Skv + key) * p.Hkv + g;
+#pragma unroll
+      for (int kk = 0; kk < C::KQ; kk++) kr[kk] = *(const s8v *)(p.k + r * DQK + 32 * kk + 8 * g16);
+#pragma unroll
+      for (int kk = 0; kk < C::KV; kk++) vr[kk] = *(const s8v *)(p.v + r * p.v_ld + 32 * kk + 8 * g16);
+    }
+    const int swq = sk_sw<DQK>(i16), swv = sk_sw<DV>(i16);
+    // dK blocks [ks0, ks0 + NKS) of step t-1, added at the start of step t.
+    const int ks0 = C::NQ - 2 * C::NKS + C::NKS * w;
+    f16v aks[C::NKS];
+#pragma unroll
+    for (int u = 0; u < C::NKS; u++) aks[u] = f16v{};
+    __syncthreads();  // the first step's tiles landed
+    int b3 = 0, hb = 0;
+    for (int t = 0; t <= nsteps; t++) {
+      if (t > 0) {
+        const int bp = b3 == 0 ? 2 : b3 - 1, sbp = (t - 1) & 1;
+        const s8v da = *(const s8v *)&st_ds[sbp][0][lo * C::HB + 8 * hi];
+        const s8v dl2 = SPLIT ? *(const s8v *)&st_ds[sbp][NH - 1][lo * C::HB + 8 * hi] : s8v{};
+        s8v bb[C::NKS];
+#pragma unroll
+        for (int u = 0; u < C::NKS; u++) bb[u] = trB(q_s[bp], true, ks0 + u);
+#pragma unroll
+        for (int u = 0; u < C::NKS; u++) aks[u] = TT::mfma(da, bb[u], aks[u]);
         if (SPLIT) {
-          st_p[1][key * C::HB + head] = TT::cvt(pr - TT::tof(ph));
-          st_ds[1][key * C::HB + head] = TT::cvt(ds - TT::tof(dh));
-        }
-      }
-    }
-    __syncthreads();  // P^T, dS^T of the whole step visible
-    // dV += P^T dO and dK += dS^T Q: M = 32 keys, N = 32-wide d blocks, K = 32 heads in two
-    // 16-steps; A = the staging row of key lo (natural read), B = transposed reads of the tiles.
-    {
-      s8v pa[2], pl[2], da[2], dl2[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
-        pa[ks] = *(const s8v *)&st_p[0][lo * C::HB + 16 * ks + 8 * hi];
-        da[ks] = *(const s8v *)&st_ds[0][lo * C::HB + 16 * ks + 8 * hi];
-        pl[ks] = SPLIT ? *(const s8v *)&st_p[1][lo * C::HB + 16 * ks + 8 * hi] : s8v{};
-        dl2[ks] = SPLIT ? *(const s8v *)&st_ds[1][lo * C::HB + 16 * ks + 8 * hi] : s8v{};
-      }
-      constexpr int NV = 2 * C::NVW, NK = 2 * NKW;
-      // For bf16 the lo-half product of operand n runs after the hi-half product of operand n+1,
-      // so that two products on one accumulator are never back to back.
-      s8v prev_b = s8v{};
-      int prev_n = -1;
-      auto lo_product = [&](int n, s8v bb) {
-        if (n < NV) {
-          const int ks = n / C::NVW, u = n % C::NVW;
-          av[u] = TT::mfma(pl[ks], bb, av[u]);
-        } else {
-          const int m = n - NV, ks = m / NKW, u = m % NKW;
-          if (u < kn) ak[u] = TT::mfma(dl2[ks], bb, ak[u]);
+          for (int u = 0; u < C::NKS; u++) aks[u] = TT::mfma(dl2, bb[u], aks[u]);
         }
-      };
-      ring_pipeline<NV + NK, PF>(
-          [&](int n) {
-            if (n < NV) return trB(do_s[buf], false, n / C::NVW, 4 * w + n % C::NVW);
-            const int m = n - NV;
-            return trB(q_s[buf], true, m / NKW, min(kf + m % NKW, C::NQ - 1));
-          },
-          [&](int n, s8v bb) {
-            if (n < NV) {
-              const int ks = n / C::NVW, u = n % C::NVW;
-              av[u] = TT::mfma(pa[ks], bb, av[u]);
-            } else {
-              const int m = n - NV, ks = m / NKW, u = m % NKW;
-              if (u < kn) ak[u] = TT::mfma(da[ks], bb, ak[u]);
-            }
-            if (SPLIT) {
-              if (prev_n >= 0) lo_product(prev_n, prev_b);
-              prev_n = n;
-              prev_b = bb;
-            }
-          });
-      if (SPLIT) lo_product(prev_n, prev_b);
+      }
+      if (t < nsteps) {
+        const int nh = min(C::HB, p.G - hb * C::HB);
+        // S^T and dP^T of the wave's block: B = Q / dO rows B[k = d][n = head] (natural reads of
+        // the head's row).  The S and dP products alternate, so consecutive MFMAs never wait on
+        // each other's accumulator; one ring carries the reads of both.
+        f4v sv = f4v{}, dpv = f4v{};
+        {
+          const short *qrow = &q_s[b3][i16 * DQK];
+          const short *drow = &do_s[b3][i16 * DV];
+          // order: S0 P0 S1 P1 ... S(KV-1) P(KV-1) S(KV) ... S(KQ-1)
+          auto is_s = [](int n) { return n >= 2 * C::KV || (n & 1) == 0; };
+          auto kidx = [](int n) { return n >= 2 * C::KV ? n - C::KV : n >> 1; };
+          ring_pipeline<C::KQ + C::KV, PF>(
+              [&](int n) {
+                const int kk = kidx(n);
+                return is_s(n) ? *(const s8v *)&qrow[8 * ((4 * kk + g16) ^ swq)]
+                               : *(const s8v *)&drow[8 * ((4 * kk + g16) ^ swv)];
+              },
+              [&](int n, s8v bv) {
+                if (is_s(n))
+                  sv = mfma16<TT>(kr[kidx(n)], bv, sv);
+                else
+                  dpv = mfma16<TT>(vr[kidx(n)], bv, dpv);
+              });
+        }
+        // P^T and dS^T of the block: register r is key 16*w + 4*g16 + r, head i16.
+        const float l = lse_s[b3][i16], dl = dl_s[b3][i16];
+        const bool hok = i16 < nh;
+        const int sb = t & 1;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int key = 16 * w + 4 * g16 + r;
+          const float c = (float)cnt_s[b3][key];
+          const float pr = (hok && c > 0.f) ? c * exp2f_hw(sv[r] * fac.c - l) : 0.f;
+          const float ds = ds_of<TT>(pr, dpv[r] + dl, fac);  // dl = minus delta
+          const short ph = TT::cvt(pr), dh = TT::cvt(ds);
+          st_p[sb][0][key * C::HB + i16] = ph;
+          st_ds[sb][0][key * C::HB + i16] = dh;
+          if (SPLIT) {
+            st_p[sb][NH - 1][key * C::HB + i16] = TT::cvt(pr - TT::tof(ph));
+            st_ds[sb][NH - 1][key * C::HB + i16] = TT::cvt(ds - TT::tof(dh));
+          }
+        }
+      }
+      __syncthreads();  // step t staged; step t+1's tiles landed
+      b3 = b3 == 2 ? 0 : b3 + 1;
+      hb = hb + 1 == nhb ? 0 : hb + 1;
     }
-    wait_vm0();
-    __syncthreads();  // next step's tiles landed; this step's tiles and staging consumed
+    add_blocks(std::integral_constant<int, C::NKS>{}, aks, dk_acc, DQK, ks0);
+    return;
   }
 
-  // Add the block's dV / dK (unscaled) into the f32 accumulators at Hkv: row m of a block is key
-  // j0 + 8*(r/4) + 4*hi + r%4, column 32*(block) + lo.
+  // Waves 2 and 3: accumulators (32 keys x 32-wide d blocks) dV blocks [NVW v, NVW v + NVW) and
+  // dK blocks [kf, kf + NKK).
+  const int v = w - 2;
+  f16v av[C::NVW], ak[C::NKK];
 #pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-    if (key < p.Skv) {
-      const int64_t row = ((int64_t)b * p.Skv + key) * p.Hkv + g;
+  for (int u = 0; u < C::NVW; u++) av[u] = f16v{};
 #pragma unroll
-      for (int u = 0; u < C::NVW; u++) unsafeAtomicAdd(&dv_acc[row * DV + 32 * (4 * w + u) + lo], av[u][r]);
+  for (int u = 0; u < C::NKK; u++) ak[u] = f16v{};
+  const int kf = v * C::NKK;
+
+  // Loads of a step, into registers through buffer resources: Q and dO rows of its heads through
+  // resources that end after the block's last head of the group (rows past it read as zero;
+  // their heads are masked), lse and delta of those heads, and the count row of the 32 keys.
+  // Tile slot s = 128 u + 64 v + lane is physical chunk s % C of row s / C and holds logical
+  // chunk (s % C) ^ sw(row); load u of the wave lands at byte 2048 u + 1024 v + 16 lane of the
+  // tile.  (Copies straight into LDS were measured slower here: with the scoring waves reading
+  // LDS at the same time, each took about 250 cycles to issue.)
+  uint32_t qoff[C::LQ], doff[C::LD];
 #pragma unroll
-      for (int u = 0; u < NKW; u++)
-        if (u < kn) unsafeAtomicAdd(&dk_acc[row * DQK + 32 * (kf + u) + lo], ak[u][r]);
+  for (int u = 0; u < C::LQ; u++) {
+    const int s = 128 * u + 64 * v + lane, r = s / C::CQ, ch = (s % C::CQ) ^ sk_sw<DQK>(r);
+    qoff[u] = (uint32_t)(r * DQK + 8 * ch) * 2;
+  }
+#pragma unroll
+  for (int u = 0; u < C::LD; u++) {
+    const int s = 128 * u + 64 * v + lane, r = s / C::CV, ch = (s % C::CV) ^ sk_sw<DV>(r);
+    doff[u] = (uint32_t)(r * DV + 8 * ch) * 2;
+  }
+  const uint32_t q_lds = lds_addr(&q_s[0][0]) + 1024 * v + 16 * lane, do_lds = lds_addr(&do_s[0][0]) + 1024 * v + 16 * lane;
+  struct StepLd {
+    s8v t[C::NLD];
+    uint32_t small;  // lse (wave 2) or delta (wave 3) of head `lane`, lanes < HB
+    uint32_t cw;     // wave 3: count word `lane` (two keys), lanes < BM / 2
+  };
+  auto step_ld = [&](int i, int hb0) {
+    StepLd L;
+    const int nh = min(C::HB, p.G - hb0);
+    const int64_t qrow = ((int64_t)b * p.Sq + i) * p.Hq + g * p.G + hb0;
+    const auto rq = buf_rsrc_v(p.q + qrow * DQK, (int64_t)nh * DQK * 2);
+    const auto rd = buf_rsrc_v(p.dout + qrow * DV, (int64_t)nh * DV * 2);
+#pragma unroll
+    for (int u = 0; u < C::LQ; u++) L.t[u] = buf_load16(rq, qoff[u]);
+#pragma unroll
+    for (int u = 0; u < C::LD; u++) L.t[C::LQ + u] = buf_load16(rd, doff[u]);
+    const int64_t l0 = ((int64_t)b * p.Hq + g * p.G + hb0) * p.Sq + i;
+    const auto rl = buf_rsrc_v((v == 0 ? (const float *)p.lse : (const float *)p.ndelta) + l0,
+                               ((int64_t)(nh - 1) * p.Sq + 1) * 4);
+    L.small = __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)(min(lane, C::HB - 1) * p.Sq) * 4, 0, 0);
+    L.cw = 0;
+    if (v == 1) {
+      const int64_t e0 = (((int64_t)b * p.Hkv + g) * p.Sq + i) * skv_pad + j0;
+      const int64_t ne = (int64_t)p.B * p.Hkv * p.Sq * skv_pad;
+      const auto rc = buf_rsrc_v(cnt + e0, (ne - e0) * 2);
+      L.cw = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(4 * min(lane, C::BM / 2 - 1)), 0, 0);
+    }
+    return L;
+  };
+  auto store_ld = [&](const StepLd &L, int bn) {
+#pragma unroll
+    for (int u = 0; u < C::LQ; u++)
+      *(__attribute__((address_space(3))) s8v *)(size_t)(q_lds + bn * (TQ * 2) + 2048 * u) = L.t[u];
+#pragma unroll
+    for (int u = 0; u < C::LD; u++)
+      *(__attribute__((address_space(3))) s8v *)(size_t)(do_lds + bn * (TD * 2) + 2048 * u) = L.t[C::LQ + u];
+    if (lane < C::HB) (v == 0 ? lse_s : dl_s)[bn][lane] = __builtin_bit_cast(float, L.small);
+    if (v == 1 && lane < C::BM / 2) ((uint32_t *)&cnt_s[bn][0])[lane] = L.cw;
+  };
+
+  // dV += P^T dO and dK += dS^T Q of a staged step: M = 32 keys, N = 32-wide d blocks, K = the
+  // step's 16 heads; A = the staging row of key lo (natural read), B = transposed reads of the
+  // tiles.
+  auto accumulate = [&](int bp, int sbp) {
+    const s8v pa = *(const s8v *)&st_p[sbp][0][lo * C::HB + 8 * hi];
+    const s8v da = *(const s8v *)&st_ds[sbp][0][lo * C::HB + 8 * hi];
+    const s8v pl = SPLIT ? *(const s8v *)&st_p[sbp][NH - 1][lo * C::HB + 8 * hi] : s8v{};
+    const s8v dl2 = SPLIT ? *(const s8v *)&st_ds[sbp][NH - 1][lo * C::HB + 8 * hi] : s8v{};
+    constexpr int NP = C::NVW + C::NKK;
+    // For bf16 the lo-half product of operand n runs after the hi-half product of operand n+1,
+    // so that two products on one accumulator are never back to back.
+    s8v prev_b = s8v{};
+    int prev_n = -1;
+    auto lo_product = [&](int n, s8v bb) {
+      if (n < C::NVW) {
+        av[n] = TT::mfma(pl, bb, av[n]);
+      } else {
+        const int u = n - C::NVW;
+        ak[u] = TT::mfma(dl2, bb, ak[u]);
+      }
+    };
+    ring_pipeline<NP, PF>(
+        [&](int n) {
+          if (n < C::NVW) return trB(do_s[bp], false, C::NVW * v + n);
+          return trB(q_s[bp], true, kf + n - C::NVW);
+        },
+        [&](int n, s8v bb) {
+          if (n < C::NVW) {
+            av[n] = TT::mfma(pa, bb, av[n]);
+          } else {
+            const int u = n - C::NVW;
+            ak[u] = TT::mfma(da, bb, ak[u]);
+          }
+          if (SPLIT) {
+            if (prev_n >= 0) lo_product(prev_n, prev_b);
+            prev_n = n;
+            prev_b = bb;
+          }
+        });
+    if (SPLIT) lo_product(prev_n, prev_b);
+  };
+
+  // Step 0's tiles; the staging buffer that step 0 reads as "step -1" holds zeros, so that every
+  // step runs the same code (its products add exact zeros to the accumulators).
+  store_ld(step_ld(i_beg, 0), 0);
+  {
+    const int lt = tid - 128;
+    for (int e = 8 * lt; e < C::BM * C::HB * NH; e += 8 * 128) {
+      *(s8v *)(&st_p[1][0][0] + e) = s8v{};
+      *(s8v *)(&st_ds[1][0][0] + e) = s8v{};
     }
   }
+  __syncthreads();  // the first step's tiles and the zero staging written
+  // Step t loads step t + 1 (the last step's rows again at the end, into a buffer no one reads
+  // any more), accumulates step t - 1 while the loads are in flight, then stores the tiles.
+  // (qi, hb) = that load's step.
+  int b3 = 0, qi = i_beg, hb = 0;
+  for (int t = 0; t <= nsteps; t++) {
+    if (t + 1 < nsteps && ++hb == nhb) {
+      hb = 0;
+      qi++;
+    }
+    const int bn = b3 == 2 ? 0 : b3 + 1, bp = b3 == 0 ? 2 : b3 - 1;
+    const StepLd L = step_ld(qi, hb * C::HB);
+    sched_fence();
+    accumulate(t == 0 ? 0 : bp, (t + 1) & 1);
+    sched_fence();
+    store_ld(L, bn);
+    __syncthreads();  // step t+1's tiles stored; step t-1's tiles and staging consumed
+    b3 = bn;
+  }
+
+  add_blocks(std::integral_constant<int, C::NVW>{}, av, dv_acc, DV, C::NVW * v);
+  add_blocks(std::integral_constant<int, C::NKK>{}, ak, dk_acc, DQK, kf);
 }
 
 bool topk_count_by_rows(int skv_pad) { return (int64_t)skv_pad * 2 <= kCountRowLdsMax; }
