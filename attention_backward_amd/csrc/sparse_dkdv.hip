@@ -22,7 +22,7 @@
 //     (hi and, for bf16, lo halves);
 //   - waves 2 and 3 (accumulating) add step t-1 into dV += P^T dO and dK += dS^T Q (32x32x16
 //     products, 8 dV and 7 dK blocks of 32 columns each; the scoring waves take the last 4 dK
-//     blocks, 2 each), and load the Q / dO tiles of step t+1 through registers.
+//     blocks, 2 each), and load the Q / dO tiles of step t+1 straight into LDS.
 // Tiles go round three LDS buffers (t+1 stored, t scored, t-1 accumulated) and one barrier per
 // step hands them on.  Every LDS operand is read a few products ahead through a register ring.
 #include "common.h"
@@ -298,13 +298,14 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
   for (int u = 0; u < C::NKK; u++) ak[u] = f16v{};
   const int kf = v * C::NKK;
 
-  // Loads of a step, into registers through buffer resources: Q and dO rows of its heads through
-  // resources that end after the block's last head of the group (rows past it read as zero;
-  // their heads are masked), lse and delta of those heads, and the count row of the 32 keys.
-  // Tile slot s = 128 u + 64 v + lane is physical chunk s % C of row s / C and holds logical
-  // chunk (s % C) ^ sw(row); load u of the wave lands at byte 2048 u + 1024 v + 16 lane of the
-  // tile.  (Copies straight into LDS were measured slower here: with the scoring waves reading
-  // LDS at the same time, each took about 250 cycles to issue.)
+  // Loads of a step, straight into LDS through buffer resources: Q and dO rows of its heads
+  // through resources that end after the block's last head of the group (rows past it read as
+  // zero; their heads are masked), lse and delta of those heads, and the count row of the 32
+  // keys.  Tile slot s = 128 u + 64 v + lane is physical chunk s % C of row s / C and holds
+  // logical chunk (s % C) ^ sw(row); load u of the wave writes 1 KB at 2048 u + 1024 v of the
+  // tile.  All of a step's loads go out before its products: spread between the products they
+  // took 12% longer, and loads through registers 13% longer (each wave's register loads came
+  // back about two steps after issue).
   uint32_t qoff[C::LQ], doff[C::LD];
 #pragma unroll
   for (int u = 0; u < C::LQ; u++) {
@@ -316,44 +317,33 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
     const int s = 128 * u + 64 * v + lane, r = s / C::CV, ch = (s % C::CV) ^ sk_sw<DV>(r);
     doff[u] = (uint32_t)(r * DV + 8 * ch) * 2;
   }
-  const uint32_t q_lds = lds_addr(&q_s[0][0]) + 1024 * v + 16 * lane, do_lds = lds_addr(&do_s[0][0]) + 1024 * v + 16 * lane;
+  const uint32_t q_lds = lds_addr(&q_s[0][0]) + 1024 * v, do_lds = lds_addr(&do_s[0][0]) + 1024 * v;
+  const uint32_t lse_lds = lds_addr(&lse_s[0][0]), dl_lds = lds_addr(&dl_s[0][0]), cnt_lds = lds_addr(&cnt_s[0][0]);
   struct StepLd {
-    s8v t[C::NLD];
-    uint32_t small;  // lse (wave 2) or delta (wave 3) of head `lane`, lanes < HB
-    uint32_t cw;     // wave 3: count word `lane` (two keys), lanes < BM / 2
+    i4v rq, rd;
   };
-  auto step_ld = [&](int i, int hb0) {
-    StepLd L;
+  auto step_ld = [&](int i, int hb0, int bn) {
     const int nh = min(C::HB, p.G - hb0);
     const int64_t qrow = ((int64_t)b * p.Sq + i) * p.Hq + g * p.G + hb0;
-    const auto rq = buf_rsrc_v(p.q + qrow * DQK, (int64_t)nh * DQK * 2);
-    const auto rd = buf_rsrc_v(p.dout + qrow * DV, (int64_t)nh * DV * 2);
-#pragma unroll
-    for (int u = 0; u < C::LQ; u++) L.t[u] = buf_load16(rq, qoff[u]);
-#pragma unroll
-    for (int u = 0; u < C::LD; u++) L.t[C::LQ + u] = buf_load16(rd, doff[u]);
     const int64_t l0 = ((int64_t)b * p.Hq + g * p.G + hb0) * p.Sq + i;
-    const auto rl = buf_rsrc_v((v == 0 ? (const float *)p.lse : (const float *)p.ndelta) + l0,
-                               ((int64_t)(nh - 1) * p.Sq + 1) * 4);
-    L.small = __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)(min(lane, C::HB - 1) * p.Sq) * 4, 0, 0);
-    L.cw = 0;
-    if (v == 1) {
+    if (v == 0) {
+      const i4v rl = buf_rsrc((const float *)p.lse + l0, ((uint64_t)(nh - 1) * p.Sq + 1) * 4);
+      if (lane < C::HB) b2lds4_at(rl, (uint32_t)(lane * p.Sq) * 4, lse_lds + bn * (C::HB * 4));
+    } else {
+      const i4v rl = buf_rsrc((const float *)p.ndelta + l0, ((uint64_t)(nh - 1) * p.Sq + 1) * 4);
+      if (lane < C::HB) b2lds4_at(rl, (uint32_t)(lane * p.Sq) * 4, dl_lds + bn * (C::HB * 4));
       const int64_t e0 = (((int64_t)b * p.Hkv + g) * p.Sq + i) * skv_pad + j0;
       const int64_t ne = (int64_t)p.B * p.Hkv * p.Sq * skv_pad;
-      const auto rc = buf_rsrc_v(cnt + e0, (ne - e0) * 2);
-      L.cw = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(4 * min(lane, C::BM / 2 - 1)), 0, 0);
+      const i4v rc = buf_rsrc(cnt + e0, (uint64_t)(ne - e0) * 2);
+      if (lane < C::BM / 2) b2lds4_at(rc, (uint32_t)(4 * lane), cnt_lds + bn * (C::BM * 2));
     }
-    return L;
+    return StepLd{buf_rsrc(p.q + qrow * DQK, (uint64_t)nh * DQK * 2), buf_rsrc(p.dout + qrow * DV, (uint64_t)nh * DV * 2)};
   };
-  auto store_ld = [&](const StepLd &L, int bn) {
-#pragma unroll
-    for (int u = 0; u < C::LQ; u++)
-      *(__attribute__((address_space(3))) s8v *)(size_t)(q_lds + bn * (TQ * 2) + 2048 * u) = L.t[u];
-#pragma unroll
-    for (int u = 0; u < C::LD; u++)
-      *(__attribute__((address_space(3))) s8v *)(size_t)(do_lds + bn * (TD * 2) + 2048 * u) = L.t[C::LQ + u];
-    if (lane < C::HB) (v == 0 ? lse_s : dl_s)[bn][lane] = __builtin_bit_cast(float, L.small);
-    if (v == 1 && lane < C::BM / 2) ((uint32_t *)&cnt_s[bn][0])[lane] = L.cw;
+  auto load_u = [&](const StepLd &L, int bn, int u) {
+    if (u < C::LQ)
+      b2lds16_at(L.rq, qoff[u], q_lds + bn * (TQ * 2) + 2048 * u);
+    else
+      b2lds16_at(L.rd, doff[u - C::LQ], do_lds + bn * (TD * 2) + 2048 * (u - C::LQ));
   };
 
   // dV += P^T dO and dK += dS^T Q of a staged step: M = 32 keys, N = 32-wide d blocks, K = the
@@ -400,18 +390,20 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
 
   // Step 0's tiles; the staging buffer that step 0 reads as "step -1" holds zeros, so that every
   // step runs the same code (its products add exact zeros to the accumulators).
-  store_ld(step_ld(i_beg, 0), 0);
   {
+    const StepLd L = step_ld(i_beg, 0, 0);
+#pragma unroll
+    for (int u = 0; u < C::NLD; u++) load_u(L, 0, u);
     const int lt = tid - 128;
     for (int e = 8 * lt; e < C::BM * C::HB * NH; e += 8 * 128) {
       *(s8v *)(&st_p[1][0][0] + e) = s8v{};
       *(s8v *)(&st_ds[1][0][0] + e) = s8v{};
     }
   }
-  __syncthreads();  // the first step's tiles and the zero staging written
+  wait_vm0();
+  __syncthreads();  // the first step's tiles landed, the zero staging written
   // Step t loads step t + 1 (the last step's rows again at the end, into a buffer no one reads
-  // any more), accumulates step t - 1 while the loads are in flight, then stores the tiles.
-  // (qi, hb) = that load's step.
+  // any more) and accumulates step t - 1.  (qi, hb) = that load's step.
   int b3 = 0, qi = i_beg, hb = 0;
   for (int t = 0; t <= nsteps; t++) {
     if (t + 1 < nsteps && ++hb == nhb) {
@@ -419,12 +411,12 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
       qi++;
     }
     const int bn = b3 == 2 ? 0 : b3 + 1, bp = b3 == 0 ? 2 : b3 - 1;
-    const StepLd L = step_ld(qi, hb * C::HB);
-    sched_fence();
+    const StepLd L = step_ld(qi, hb * C::HB, bn);
+#pragma unroll
+    for (int u = 0; u < C::NLD; u++) load_u(L, bn, u);
     accumulate(t == 0 ? 0 : bp, (t + 1) & 1);
-    sched_fence();
-    store_ld(L, bn);
-    __syncthreads();  // step t+1's tiles stored; step t-1's tiles and staging consumed
+    wait_vm0();
+    __syncthreads();  // step t+1's tiles landed; step t-1's tiles and staging consumed
     b3 = bn;
   }
 
