@@ -62,8 +62,8 @@ PROFILED_TRAFFIC = {
         fetch_kib=76850.5, write_kib=33280.0, fetch_scale=2.000, write_scale=1.000,
         files=("dense_fwd.hip", "common.h"), sha="740a012af4d2d2b7"),
     ("sparse_dkdv", "sparse_mla_b1_sq4096_skv8192_h64_dqk576_dv512_top2048_bf16"): dict(
-        fetch_kib=7803191.4, write_kib=217600.0, fetch_scale=2.000, write_scale=1.000,
-        files=("sparse_dkdv.hip", "common.h"), sha="5253a91935b180a2"),
+        fetch_kib=7178644.6, write_kib=426496.0, fetch_scale=2.000, write_scale=1.000,
+        files=("sparse_dkdv.hip", "common.h"), sha="bd12bbc3fd015437"),
 }
 
 
