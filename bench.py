@@ -248,6 +248,33 @@ def gpu_state():
         return None
 
 
+def gemm_clock(n: int, reps: int = 20):
+    """A plain library GEMM (torch.matmul, fp16, n x n x n, contiguous operands) on three operand
+    sets -- zeros, a constant, N(0,1) -- each timed with events: the matrix cores' throughput
+    and, under the profiler's GRBM_GUI_ACTIVE counter, their clock as a function of the data."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    cases = (("zeros", lambda: torch.zeros(n, n, dtype=torch.float16, device=dev)),
+             ("constant 1/64", lambda: torch.full((n, n), 1.0 / 64, dtype=torch.float16, device=dev)),
+             ("normal(0,1)", lambda: torch.randn(n, n, generator=g, dtype=torch.float16, device=dev)))
+    for name, make in cases:
+        a, b = make(), make()
+        c = torch.empty(n, n, dtype=torch.float16, device=dev)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        print(json.dumps({"gemm": f"{n}x{n}x{n} fp16", "operands": name, "ms": round(ms, 4),
+                          "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}), flush=True)
+        del a, b, c
+
+
 def calib_copy(args, dev):
     """After timing: one fp16 -> f32 device copy reading --calib-copy-mib MiB, a known-size kernel
     against which profiler byte counters are scaled (a conversion, so it runs an elementwise
@@ -474,7 +501,13 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one fp16->f32 device copy reading this many MiB (a known-size "
                          "kernel against which profiler byte counters are scaled)")
+    ap.add_argument("--gemm-clock", type=int, default=0,
+                    help="instead of a workload: time an n x n x n fp16 library GEMM on zero, constant and "
+                         "random operands (the matrix cores' throughput as a function of the data)")
     args = ap.parse_args()
+    if args.gemm_clock:
+        gemm_clock(args.gemm_clock)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the backward runs on one GPU and this library has no "
               "multi-GPU path (it would shard by (batch, head) or by query rows); run it with --gpus 1.",
