@@ -303,9 +303,9 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
   // zero; their heads are masked), lse and delta of those heads, and the count row of the 32
   // keys.  Tile slot s = 128 u + 64 v + lane is physical chunk s % C of row s / C and holds
   // logical chunk (s % C) ^ sw(row); load u of the wave writes 1 KB at 2048 u + 1024 v of the
-  // tile.  All of a step's loads go out before its products: spread between the products they
-  // took 12% longer, and loads through registers 13% longer (each wave's register loads came
-  // back about two steps after issue).
+  // tile.  All of a step's loads go out before its products: spread between the products the
+  // kernel took 17% longer, and with loads through registers 13% longer (each wave's register
+  // loads came back about two steps after issue).
   uint32_t qoff[C::LQ], doff[C::LD];
 #pragma unroll
   for (int u = 0; u < C::LQ; u++) {
