@@ -41,6 +41,11 @@ SMALL = [
     sparse("mla_h64_fp16_two_kv", B=2, Sq=37, Skv=80, Hq=128, Hkv=2, dtype="fp16", topk=40, seed=204),
     # fp16 with G = 128: two 64-head blocks of one query row
     sparse("g128_fp16", Sq=20, Skv=45, Hq=128, Hkv=1, dtype="fp16", topk=33, seed=205),
+    # Sq = 600: each key block's queries span three dK/dV query chunks of 256 (counted from the
+    # last query: [344, 600), [88, 344), [0, 88)), whose partial blocks add into the accumulators;
+    # G = 24 ends with a ragged 8-head block; Skv = 700 ends with a ragged 28-key block
+    sparse("multi_chunk_g24_bf16", Sq=600, Skv=700, Hq=24, Hkv=1, topk=96, seed=206),
+    sparse("multi_chunk_g24_fp16", B=2, Sq=600, Skv=700, Hq=24, Hkv=1, dtype="fp16", topk=70, seed=207),
 ]
 
 
