@@ -123,17 +123,13 @@ __device__ __forceinline__ int sk_sw(int row) {
   return (2 * ROWLEN) % 256 == 0 ? swz<128>(row) : swz<64>(row);
 }
 
-#ifndef ATTN_SPARSE_DKDV_SPLIT
-#define ATTN_SPARSE_DKDV_SPLIT 1
-#endif
-
 template <class TT, int DQK, int DV>
 __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, const uint16_t *__restrict__ cnt,
                                                              int skv_pad, int qchunk, int nchunk,
                                                              float *__restrict__ dk_acc, float *__restrict__ dv_acc) {
   using C = SkCfg<DQK, DV>;
   constexpr int PF = 3;
-  constexpr bool SPLIT = TT::SPLIT && ATTN_SPARSE_DKDV_SPLIT;
+  constexpr bool SPLIT = TT::SPLIT;
   constexpr int NH = SPLIT ? 2 : 1;                   // staged halves of P^T and dS^T
   constexpr int TQ = C::HB * DQK, TD = C::HB * DV;    // elements per Q / dO tile
   __shared__ __attribute__((aligned(16))) short q_s[3][TQ];
@@ -171,6 +167,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dkdv_kernel(const Params p, con
   // 2 and 3 meanwhile add step t-1 into dV and dK and load the tiles of step t+1.  The tiles go
   // round three buffers (t+1 loading, t scored, t-1 accumulated), the staging round two, and
   // one barrier per step hands both on.  The loop runs one extra step to accumulate the last.
+
   // Transposed read of B[k = head][n = d] from a [head][d] tile (heads 8*hi + e).
   auto trB = [&](const short *tile, bool is_q, int nb) {
     const int rowlen = is_q ? DQK : DV;

@@ -63,7 +63,7 @@ PROFILED_TRAFFIC = {
         files=("dense_fwd.hip", "common.h"), sha="740a012af4d2d2b7"),
     ("sparse_dkdv", "sparse_mla_b1_sq4096_skv8192_h64_dqk576_dv512_top2048_bf16"): dict(
         fetch_kib=7178644.6, write_kib=426496.0, fetch_scale=2.000, write_scale=1.000,
-        files=("sparse_dkdv.hip", "common.h"), sha="3a206334ef31372b"),
+        files=("sparse_dkdv.hip", "common.h"), sha="3dcaa90113c98a4e"),
 }
 
 
